@@ -1,0 +1,178 @@
+"""Training throughput of the GPT-2 124M step (bf16, fp32 master weights and
+AdamW moments, B=16, T=1024) on one MI355X, through the C ABI.
+
+One step = forward (with the mean loss) + backward + AdamW update, on seeded
+synthetic Zipf(1.1) tokens, inputs resident in HBM before timing starts.
+Prints one JSON line: tokens/s, MFU against the bf16 dense peak, the dominant
+kernel class against its roofline (HIP-event durations measured in the timed
+steps), and the CPU oracle timed on a bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_FLOPS = 2.5e15   # MI355X dense bf16 MFMA, published
+PEAK_HBM_BYTES = 8.0e12    # MI355X HBM3E, published
+WORKLOAD = "gpt2_124m"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(w, T_sample=256):
+    """The oracle (fp64, plain loops, OpenMP over independent outputs) on one
+    sequence of T_sample tokens of the same model: one full training step."""
+    import oracle
+    from oracle.wrapper import Oracle
+    from transformer_lm_amd import synth
+    oracle.build(force=False)
+    ws = w.with_batch(B=1, T=T_sample, steps=1)
+    p = synth.init_params(ws)
+    x, y = synth.split_batch(synth.tokens(ws)[0])
+    threads = len(os.sched_getaffinity(0))
+    o = Oracle(ws, p, threads=threads)
+    t0 = time.perf_counter()
+    o.forward(x, y)
+    o.backward()
+    o.update(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, 1)
+    dt = time.perf_counter() - t0
+    cores = o.lib.oracle_get_threads()
+    o.close()
+    return {"value": ws.BT / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"one training step (fwd+bwd+AdamW) of the same 124M model on 1 sequence "
+                      f"of {T_sample} tokens, fp64 oracle, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default=WORKLOAD)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the step is a single-GPU hot path with no collectives)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from transformer_lm_amd import gpt2, synth
+    from transformer_lm_amd.workloads import WORKLOADS
+
+    w = WORKLOADS[args.workload]
+    total = args.warmup + args.steps
+    log(f"[bench] {w.name}: B={w.B} T={w.T} C={w.C} L={w.L} dtype={w.dtype}; "
+        f"{args.warmup} warmup + {args.steps} timed steps")
+    params = synth.init_params(w)
+    toks = synth.tokens(w, steps=max(total, 1))
+    dev_in = [torch.from_numpy(np.ascontiguousarray(toks[s][:, :-1])).cuda() for s in range(total)]
+    dev_tg = [torch.from_numpy(np.ascontiguousarray(toks[s][:, 1:])).cuda() for s in range(total)]
+    model = gpt2.GPT2(gpt2.config(w), params)
+    stream = model.stream
+    loss_dev = torch.zeros(total, dtype=torch.float32, device="cuda")
+    loss_view = model.act("loss")
+
+    def step(s):
+        model.forward(dev_in[s], dev_tg[s], want_loss=False)
+        loss_dev[s].copy_(loss_view[0])
+        model.backward()
+        model.update(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, s + 1)
+
+    # warmup: one step (the second, if there are two) records every kernel
+    # class to find the dominant one
+    pidx = 1 if args.warmup >= 2 else 0
+    for s in range(args.warmup):
+        if s == pidx:
+            model.timing_arm("", 8192)
+        step(s)
+        if s == pidx:
+            prof = model.timing_read()
+            model.timing_arm(None)
+    torch.cuda.synchronize()
+    if args.warmup == 0:
+        prof = {}
+    dominant = max(prof, key=lambda k: prof[k][1]) if prof else "matmul"
+    for k, (n, ms, wk, isb) in sorted(prof.items(), key=lambda kv: -kv[1][1]):
+        rate = wk / (ms * 1e-3) / (1e9 if isb else 1e12)
+        log(f"[bench] warmup profile {k:15s} {n:4d} launches {ms:9.3f} ms  "
+            f"{rate:8.1f} {'GB/s' if isb else 'TFLOP/s'}")
+
+    # timed region: events bracket only the dominant class's launches
+    model.timing_arm(dominant, 4096)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for s in range(args.warmup, total):
+        step(s)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    dom = model.timing_read().get(dominant)
+    losses = loss_dev.cpu().tolist()
+
+    ms_per_step = wall * 1e3 / max(args.steps, 1)
+    tok_s = w.BT * args.steps / wall
+    mfu = tok_s * w.flops_per_token() / PEAK_BF16_FLOPS
+    log(f"[bench] {ms_per_step:.2f} ms/step (events {gpu_ms / max(args.steps, 1):.2f}), "
+        f"{tok_s:,.0f} tokens/s, MFU {100 * mfu:.2f}%")
+    log("[bench] loss per step: " + " ".join(f"{v:.4f}" for v in losses))
+
+    roofline = None
+    if dom:
+        n, ms, wk, isb = dom
+        achieved = wk / (ms * 1e-3)
+        peak = PEAK_HBM_BYTES if isb else PEAK_BF16_FLOPS
+        unit_div = 1e9 if isb else 1e12
+        roofline = {"kernel": dominant, "bound": "hbm" if isb else "mfma",
+                    "achieved": round(achieved / unit_div, 2), "peak": peak / unit_div,
+                    "unit": "GB/s" if isb else "TFLOP/s", "frac": round(achieved / peak, 4),
+                    "traffic": None, "launches": n, "avg_launch_ms": round(ms / n, 4)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample ...")
+        cpu = cpu_baseline(w)
+        log(f"[bench] cpu baseline: {cpu['value']:.1f} tokens/s on {cpu['cores']} threads")
+
+    out = {
+        "metric": "train tokens/s, GPT-2 124M bf16 B=16 T=1024, 1 MI355X; MFU %",
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded Zipf(1.1) tokens over 50257 ids, seeded N(0,0.02) init",
+        "config": {"workload": f"GPT-2 124M training step (forward, backward, AdamW), bf16 "
+                               f"activations with fp32 master weights and moments, "
+                               f"B={w.B} T={w.T}",
+                   "global_batch": w.B, "seq_len": w.T, "parallelism": "single GPU"},
+        "mfu": round(mfu, 4),
+        "flops_per_token": w.flops_per_token(),
+        "loss_first_last": [round(losses[0], 4), round(losses[-1], 4)] if losses else None,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

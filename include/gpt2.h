@@ -1,0 +1,174 @@
+/*
+ * gpt2.h -- C ABI of libgpt2.so: one GPT-2 training step on an MI355X (gfx950).
+ *
+ * The step is GPT-2 as llm.c trains it: the forward pass "from the matrix
+ * multiply up", every gradient derived by hand, and AdamW (page "Building
+ * GPT-2 from scratch", exercise table rows A1 and A2). Tensors are flat
+ * row-major arrays addressed by explicit offsets (page "llm.c: Large Language
+ * Model Training in Pure C/CUDA Without Dependencies", section "Tensor Memory
+ * Layout"), and all memory is planned up front in single blobs so that a step
+ * can never run out of memory later (talk "llm.c's Origin and the Future of
+ * LLM Compilers", statement on allocating everything in a single blob).
+ *
+ * Memory model. The caller allocates and owns two device buffers, sized by
+ * gpt2_param_buffer_bytes() and gpt2_act_buffer_bytes(), plus the token
+ * buffers and the stream; all must outlive the handle. The library allocates
+ * no device memory at all; it owns only the small host-side handle.
+ *
+ * Parameter buffer: five regions, each 256-byte aligned, each holding the N
+ * parameters in the tensor order of gpt2_param_table():
+ *   GPT2_REGION_MASTER      N fp32   parameters (the master copy)
+ *   GPT2_REGION_GRAD        N fp32   dLoss/dparameter from gpt2_backward
+ *   GPT2_REGION_M           N fp32   AdamW first moment
+ *   GPT2_REGION_V           N fp32   AdamW second moment
+ *   GPT2_REGION_PARAM_BF16  N bf16   working copy read by the bf16 forward
+ *                                    (bf16 mode only; absent in fp32 mode)
+ * Inside a region, weights are stored (out, in) row-major, so a linear layer
+ * is y = x W^T + b; qkvw holds the row blocks [Q; K; V] and head h owns rows
+ * h*hs .. h*hs+hs-1 of each block.
+ *
+ * Precision. dtype GPT2_DTYPE_FP32: everything fp32. GPT2_DTYPE_BF16:
+ * activations, activation gradients and the working parameter copy are bf16
+ * (round to nearest even); master weights, parameter gradients, AdamW moments,
+ * LayerNorm statistics, losses and every accumulation are fp32.
+ *
+ * Calls are asynchronous on the handle's HIP stream, except gpt2_create (it
+ * synchronises after uploading parameters) and gpt2_forward with a non-null
+ * h_loss (it synchronises to read the loss). A handle is not thread-safe.
+ *
+ * Errors: every int-returning call returns GPT2_OK or a negative code;
+ * gpt2_last_error() describes the most recent failure on the calling thread.
+ * Host-side validation happens at the call. Token ids are checked on the
+ * device: an id outside [0, V) sets a flag (the offending position reads as
+ * zero) that the next synchronising call reports as GPT2_ETOKEN.
+ */
+#ifndef GPT2_H
+#define GPT2_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct gpt2_config {
+    int32_t V;      /* real vocabulary size                                   */
+    int32_t Vp;     /* padded vocabulary: rows of wte, columns of the logits; */
+                    /* a multiple of 64, >= V                                 */
+    int32_t max_T;  /* rows of wpe                                            */
+    int32_t C;      /* channels: a multiple of 8, at most 2048                */
+    int32_t L;      /* layers                                                 */
+    int32_t NH;     /* heads: C % NH == 0, head size C/NH a multiple of 8,    */
+                    /* at most 128                                            */
+    int32_t B;      /* batch rows per step                                    */
+    int32_t T;      /* sequence length, 1 <= T <= max_T                       */
+    int32_t dtype;  /* GPT2_DTYPE_FP32 or GPT2_DTYPE_BF16                     */
+} gpt2_config;
+
+typedef struct gpt2 gpt2; /* opaque, host-side handle */
+
+enum {
+    GPT2_OK = 0,
+    GPT2_EINVAL = -1, /* null or misaligned pointer, bad argument        */
+    GPT2_ESHAPE = -2, /* inconsistent configuration                      */
+    GPT2_EHIP = -3,   /* a HIP runtime call failed                       */
+    GPT2_ESTATE = -4, /* call out of order (backward without a forward   */
+                      /* that had targets)                               */
+    GPT2_ETOKEN = -5  /* a token id outside [0, V) was seen on the device */
+};
+
+enum { GPT2_DTYPE_FP32 = 0, GPT2_DTYPE_BF16 = 1 };
+
+enum {
+    GPT2_REGION_MASTER = 0,
+    GPT2_REGION_GRAD = 1,
+    GPT2_REGION_M = 2,
+    GPT2_REGION_V = 3,
+    GPT2_REGION_PARAM_BF16 = 4
+};
+
+/* Number of parameters N (elements of each region); -1 if cfg is invalid. */
+int64_t gpt2_num_params(const gpt2_config* cfg);
+
+/* Number of parameter tensors in the flat layout (16). */
+int gpt2_num_param_tensors(void);
+
+/* Tensor i of the flat layout (storage order): its name (static string),
+ * element offset inside a region, number of dimensions and shape. */
+int gpt2_param_table(const gpt2_config* cfg, int i, const char** name, int64_t* offset,
+                     int32_t* ndim, int32_t shape[3]);
+
+/* Bytes the caller must allocate for the parameter and activation buffers;
+ * -1 if cfg is invalid. Both buffers must be 256-byte aligned. */
+int64_t gpt2_param_buffer_bytes(const gpt2_config* cfg);
+int64_t gpt2_act_buffer_bytes(const gpt2_config* cfg);
+
+/* Binds a handle to the caller's buffers and stream (a hipStream_t; NULL is
+ * the null stream). If h_init_params (N fp32 values on the host) is non-null
+ * it is uploaded as the master parameters; otherwise the master region must
+ * already hold them. Derives the bf16 copy (bf16 mode), zeroes the moments
+ * and the gradients, and synchronises. */
+int gpt2_create(const gpt2_config* cfg, void* d_param_buf, void* d_act_buf,
+                const float* h_init_params, void* hip_stream, gpt2** out);
+
+/* Forward pass over B*T tokens. d_inputs, d_targets: device int32 arrays of
+ * B*T ids, row-major (B, T). With targets, the per-position losses and their
+ * mean are computed and the logits buffer is overwritten in place by
+ * dLoss/dlogits (the fused classifier), ready for gpt2_backward; without
+ * targets the logits (B, T, Vp) are left in the activation buffer. If h_loss
+ * is non-null (targets required) the call synchronises and stores the mean
+ * loss there. */
+int gpt2_forward(gpt2* h, const int32_t* d_inputs, const int32_t* d_targets, float* h_loss);
+
+/* Backward pass of the mean loss of the last forward (which must have had
+ * targets). Overwrites every parameter gradient in GPT2_REGION_GRAD. */
+int gpt2_backward(gpt2* h);
+
+/* One AdamW step over the flat parameter array, t = step >= 1:
+ * m = b1 m + (1-b1) g; v = b2 v + (1-b2) g^2;
+ * theta -= lr (m/(1-b1^t) / (sqrt(v/(1-b2^t)) + eps) + weight_decay theta),
+ * then (bf16 mode) the working copy is re-rounded from theta. */
+int gpt2_update(gpt2* h, float lr, float beta1, float beta2, float eps, float weight_decay,
+                int32_t step);
+
+/* Device pointer to a parameter-buffer region (GPT2_REGION_*). */
+int gpt2_region(gpt2* h, int which, void** d_ptr);
+
+/* Device pointer and size in bytes of a named activation, for inspection:
+ * "encoded", "ln1", "ln1_mean", "ln1_rstd", "qkv", "atty", "att_lse",
+ * "residual2", "ln2", "ln2_mean", "ln2_rstd", "fch", "fch_gelu", "residual3",
+ * "lnf", "lnf_mean", "lnf_rstd", "logits", "losses", "loss". Per-layer
+ * activations are stacked (L, ...). Element type: fp32 for the statistics,
+ * "att_lse", "losses" and "loss"; the mode's activation type otherwise. */
+int gpt2_act(gpt2* h, const char* name, void** d_ptr, int64_t* bytes);
+
+/* Kernel timing, for measuring each kernel against its roofline. After
+ * gpt2_timing_arm(h, prefix, max_launches), every kernel launch whose class
+ * name starts with `prefix` ("" = every launch; NULL disarms) is bracketed by
+ * a pair of HIP events on the handle's stream, for up to max_launches
+ * launches; arming discards earlier records. Classes: "encoder_fwd",
+ * "layernorm_fwd", "matmul_fwd", "attention_fwd", "gelu_fwd", "classifier",
+ * "matmul_bwd_dx", "matmul_bwd_dw", "bias_bwd", "gelu_bwd", "layernorm_bwd",
+ * "attention_bwd", "encoder_bwd", "adamw". The events are created at arming
+ * (no device memory is allocated). */
+int gpt2_timing_arm(gpt2* h, const char* prefix, int32_t max_launches);
+
+/* Per-class totals over the recorded launches; synchronises the stream.
+ * Class i in [0, gpt2_timing_classes()): its name, launch count, summed event
+ * time in ms, and summed algorithmic work with its unit (work_is_bytes = 0:
+ * floating-point operations; 1: compulsory HBM bytes at the stored types). */
+int gpt2_timing_classes(void);
+int gpt2_timing_read(gpt2* h, int i, const char** name, int64_t* launches, double* total_ms,
+                     double* work, int32_t* work_is_bytes);
+
+/* Releases the handle (not the caller's buffers). NULL is accepted. */
+void gpt2_free(gpt2* h);
+
+/* Message for the most recent failure on this thread ("" if none). */
+const char* gpt2_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GPT2_H */

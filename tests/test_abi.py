@@ -1,0 +1,91 @@
+"""The C-ABI library: it loads, exports every entry point include/gpt2.h
+declares, and its host-side planning and validation behave. No kernel runs."""
+import ctypes as ct
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def g():
+    from transformer_lm_amd import build
+    if not build.is_built():
+        build.build()
+    from transformer_lm_amd import gpt2
+    return gpt2
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "gpt2.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gpt2_\w+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported(g):
+    names = declared_functions()
+    assert len(names) == 16
+    lib = ct.CDLL(g.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(g.EXPORTS) == names
+
+
+def test_param_layout_matches_the_generator(g):
+    from transformer_lm_amd.workloads import WORKLOADS, param_offsets
+    for name in ("tiny", "tiny_pad", "gpt2_124m", "gpt2_350m", "gpt2_1558m"):
+        w = WORKLOADS[name]
+        cfg = g.config(w)
+        assert g.num_params(cfg) == w.num_params()
+        offs = param_offsets(w)
+        tab = g.param_table(cfg)
+        assert [t[0] for t in tab] == list(offs)
+        for tname, off, shape in tab:
+            assert (off, shape) == offs[tname], tname
+
+
+def test_buffer_sizes(g):
+    from transformer_lm_amd.workloads import WORKLOADS
+    w = WORKLOADS["gpt2_124m"]
+    cfg = g.config(w)
+    n = w.num_params()
+    pb = g.param_buffer_bytes(cfg)
+    assert 18 * n <= pb <= 18 * n + 5 * 256          # 4 fp32 regions + bf16 copy
+    ab = g.act_buffer_bytes(cfg)
+    BT, C, L = w.BT, w.C, w.L
+    # the bf16 activations alone: 14 C-wide rows per layer-position + the logits
+    assert ab > 2 * (L * BT * 14 * C + BT * w.Vp)
+    assert ab < 12e9                                  # well inside 288 GB of HBM
+    w32 = WORKLOADS["tiny"]
+    assert g.param_buffer_bytes(g.config(w32)) >= 16 * w32.num_params()
+
+
+@pytest.mark.parametrize("field,value", [("C", 30), ("NH", 5), ("Vp", 60), ("T", 64),
+                                         ("dtype", 7), ("C", 4096), ("B", 0)])
+def test_invalid_configs_are_rejected(g, field, value):
+    from transformer_lm_amd.workloads import WORKLOADS
+    cfg = g.config(WORKLOADS["tiny"])
+    setattr(cfg, field, value)
+    with pytest.raises(g.GPT2Error) as e:
+        g.num_params(cfg)
+    assert e.value.code == g.GPT2_ESHAPE
+    assert g.last_error()
+
+
+def test_create_rejects_null_and_misaligned_buffers(g):
+    from transformer_lm_amd.workloads import WORKLOADS
+    cfg = g.config(WORKLOADS["tiny"])
+    h = ct.c_void_p()
+    rc = g._lib.gpt2_create(ct.byref(cfg), None, None, None, None, ct.byref(h))
+    assert rc == g.GPT2_EINVAL and not h.value
+    rc = g._lib.gpt2_create(ct.byref(cfg), 0x1004, 0x2000, None, None, ct.byref(h))
+    assert rc == g.GPT2_EINVAL and "aligned" in g.last_error()
+
+
+def test_null_handle_calls_fail_cleanly(g):
+    assert g._lib.gpt2_backward(None) == g.GPT2_EINVAL
+    assert g._lib.gpt2_update(None, 1e-3, 0.9, 0.999, 1e-8, 0.0, 1) == g.GPT2_EINVAL
+    assert g._lib.gpt2_forward(None, None, None, None) == g.GPT2_EINVAL
+    g._lib.gpt2_free(None)

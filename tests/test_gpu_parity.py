@@ -1,0 +1,214 @@
+"""GPU parity: the HIP training step through the C ABI against the CPU oracle,
+on the same seeded parameters and tokens.
+
+Tolerances (the training-step contract): encoder gather bit-exact; fp32 mode
+loss relative error <= 1e-5 and per-tensor max|dg|/max|g_ref| <= 1e-3; bf16
+mode loss within 2e-2 absolute and per-tensor gradient cosine >= 0.99.
+Reduced-depth variants of the 350M and 1.5B shapes keep their per-layer shapes
+(C, NH, head size) at sizes the oracle steps in seconds.
+"""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+
+from parity import (bf16_round, check_bf16, check_fp32, cosine, gpu_steps, oracle_steps,
+                    per_tensor, rel_err, say)
+from transformer_lm_amd import synth
+from transformer_lm_amd.workloads import WORKLOADS, param_offsets
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import oracle
+    oracle.build(force=False)
+    from transformer_lm_amd import build
+    if not build.is_built():
+        build.build()
+
+
+def _inputs(w, steps=None):
+    return synth.init_params(w), synth.tokens(w, steps=steps)
+
+
+# ---------------------------------------------------------------- encoder --
+
+@pytest.mark.parametrize("name,dtype", [("tiny", "fp32"), ("gpt2_124m_fp32", "fp32"),
+                                        ("tiny", "bf16"), ("gpt2_124m", "bf16")])
+def test_encoder_forward_is_bit_exact(name, dtype):
+    import torch
+    from transformer_lm_amd import gpt2
+    w = replace(WORKLOADS[name], dtype=dtype)
+    if name == "gpt2_124m":
+        w = w.with_batch(B=2, T=256)
+    p, toks = _inputs(w, steps=1)
+    x, y = synth.split_batch(toks[0])
+    say(f"encoder {name} {dtype} B={w.B} T={w.T}")
+    m = gpt2.GPT2(gpt2.config(w), p)
+    m.forward(torch.from_numpy(x).cuda(), torch.from_numpy(y).cuda())
+    got = m.act("encoded").float().cpu().numpy().reshape(w.B, w.T, w.C)
+    offs = param_offsets(w)
+    wte = p[offs["wte"][0]:][: w.Vp * w.C].reshape(w.Vp, w.C)
+    wpe = p[offs["wpe"][0]:][: w.max_T * w.C].reshape(w.max_T, w.C)
+    if dtype == "fp32":
+        from oracle.wrapper import Oracle
+        o = Oracle(w, p, precision="f32")
+        o.forward(x, y)
+        expect = o.act("encoded").astype(np.float32).reshape(w.B, w.T, w.C)
+    else:
+        # one fp32 add of the two bf16 embeddings, rounded to bf16
+        expect = bf16_round(bf16_round(wte)[x] + bf16_round(wpe)[None, :w.T])
+    assert np.array_equal(got, expect)
+
+
+# -------------------------------------------------------------- fp32 step --
+
+@pytest.mark.parametrize("name", ["tiny", "tiny_pad", "gpt2_124m_fp32"])
+def test_fp32_step_matches_oracle(name):
+    w = WORKLOADS[name]
+    p, toks = _inputs(w)
+    say(f"fp32 step {name}")
+    gpu = gpu_steps(w, p, toks, 1)
+    ref = oracle_steps(w, p, toks, 1)
+    rep = check_fp32(w, gpu, ref)
+    say({k: f"{v:.2e}" for k, v in rep.items()})
+    # after the update: m and v are linear / quadratic in g
+    assert rel_err(gpu["m"], ref["m"]) <= 1e-3
+    assert rel_err(gpu["v"], ref["v"]) <= 2e-3
+    # theta: at t = 1 the step is lr * g / (|g| + eps), which may flip for
+    # near-zero gradients; elsewhere it must agree to well under lr
+    g = ref["grads"][1]
+    dth = np.abs(gpu["params"] - ref["params"])
+    small = np.zeros_like(g, dtype=bool)
+    for n, gt in per_tensor(w, g).items():
+        off, s = param_offsets(w)[n]
+        small[off:off + gt.size] = np.abs(gt) < 1e-3 * np.abs(gt).max()
+    assert dth[small].max(initial=0) <= 2 * w.lr
+    assert dth[~small].max() <= 1e-4 * w.lr + 1e-6 * np.abs(ref["params"]).max()
+
+
+@pytest.mark.parametrize("name", ["tiny", "gpt2_124m_fp32"])
+def test_fp32_intermediates_match_oracle(name):
+    """Forward activations in dependency order: the first to fail is the bug."""
+    import torch
+    from oracle.wrapper import Oracle
+    from transformer_lm_amd import gpt2
+    w = WORKLOADS[name]
+    p, toks = _inputs(w)
+    x, y = synth.split_batch(toks[0])
+    say(f"fp32 intermediates {name}")
+    m = gpt2.GPT2(gpt2.config(w), p)
+    xd, yd = torch.from_numpy(x).cuda(), torch.from_numpy(y).cuda()
+    m.forward(xd)                       # no targets: the logits stay
+    torch.cuda.synchronize()
+    o = Oracle(w, p)
+    o.forward(x, y)
+    for act in ("encoded", "ln1", "ln1_mean", "ln1_rstd", "qkv", "atty", "residual2", "ln2",
+                "fch", "fch_gelu", "residual3", "lnf", "logits"):
+        got = m.act(act).double().cpu().numpy()
+        ref = o.act(act)
+        e = rel_err(got[: ref.size], ref)
+        say(f"  {act}: {e:.2e}")
+        assert e <= 1e-4, act
+    m.forward(xd, yd)
+    losses = m.act("losses").double().cpu().numpy()
+    assert rel_err(losses, o.act("losses")) <= 1e-5
+    dz = m.act("logits").double().cpu().numpy().reshape(w.BT, w.Vp)
+    assert not dz[:, w.V:].any()                              # padded columns
+    assert np.abs(dz.sum(1)).max() <= 1e-6 / w.BT * 100       # sum_v dlogits = 0
+
+
+# -------------------------------------------------------------- bf16 step --
+
+def _bf16_cases():
+    return [
+        ("tiny_bf16", replace(WORKLOADS["tiny"], dtype="bf16", steps=3)),
+        ("tiny_pad_bf16", replace(WORKLOADS["tiny_pad"], dtype="bf16", steps=2)),
+        ("gpt2_124m_B2T64", WORKLOADS["gpt2_124m"].with_batch(B=2, T=64, steps=2)),
+        ("gpt2_350m_L2_B1T128", replace(WORKLOADS["gpt2_350m"], L=2, B=1, T=128, steps=2)),
+        ("gpt2_1558m_L2_B1T64", replace(WORKLOADS["gpt2_1558m"], L=2, B=1, T=64, steps=2)),
+    ]
+
+
+@pytest.mark.parametrize("case", _bf16_cases(), ids=[c[0] for c in _bf16_cases()])
+def test_bf16_steps_match_oracle(case):
+    name, w = case
+    p, toks = _inputs(w)
+    say(f"bf16 steps {name} ({w.steps} steps)")
+    gpu = gpu_steps(w, p, toks, w.steps)
+    ref = oracle_steps(w, p, toks, w.steps, threads=16)
+    rep = check_bf16(w, gpu, ref)
+    say({k: (f"{v:.4f}") for k, v in rep.items()})
+
+
+def test_bf16_full_size_sampled_losses():
+    """The 124M bf16 step at B=16, T=1024 (the timed configuration): the
+    per-position losses of two sampled sequences against the oracle's forward
+    on those sequences alone, plus properties that hold at any size."""
+    import torch
+    from oracle.wrapper import Oracle
+    from transformer_lm_amd import gpt2
+    w = WORKLOADS["gpt2_124m"]
+    p, toks = _inputs(w, steps=1)
+    x, y = synth.split_batch(toks[0])
+    say("bf16 full size 124M B=16 T=1024")
+    m = gpt2.GPT2(gpt2.config(w), p)
+    loss = m.forward(torch.from_numpy(x).cuda(), torch.from_numpy(y).cuda())
+    losses = m.act("losses").double().cpu().numpy().reshape(w.B, w.T)
+    m.backward()
+    g = m.region(gpt2.REGION_GRAD).double().cpu().numpy()
+    assert np.isfinite(loss) and np.all(np.isfinite(g))
+    assert abs(loss - losses.mean()) < 1e-4
+    gt = per_tensor(w, g)
+    assert not gt["wte"].reshape(w.Vp, w.C)[w.V:].any()      # padded vocab rows
+    for b in (0, w.B - 1):
+        ws = w.with_batch(B=1)
+        o = Oracle(ws, p, threads=16)
+        o.forward(x[b:b + 1], y[b:b + 1])
+        ref = o.act("losses")
+        d = np.abs(losses[b] - ref)
+        say(f"  seq {b}: mean {losses[b].mean():.4f} vs {ref.mean():.4f}, max|d| {d.max():.3f}")
+        assert abs(losses[b].mean() - ref.mean()) <= 2e-2
+        o.close()
+
+
+def test_steps_are_deterministic():
+    w = WORKLOADS["gpt2_124m"].with_batch(B=2, T=128, steps=1)
+    p, toks = _inputs(w)
+    say("determinism 124M bf16 B=2 T=128")
+    a = gpu_steps(w, p, toks, 1, want=("params",))
+    b = gpu_steps(w, p, toks, 1, want=("params",))
+    assert a["losses"] == b["losses"]
+    assert np.array_equal(a["grads"][1], b["grads"][1])
+    assert np.array_equal(a["params"], b["params"])
+
+
+def test_error_paths():
+    import torch
+    from transformer_lm_amd import gpt2
+    w = WORKLOADS["tiny_pad"]
+    p, toks = _inputs(w)
+    x, y = synth.split_batch(toks[0])
+    say("error paths tiny_pad")
+    m = gpt2.GPT2(gpt2.config(w), p)
+    with pytest.raises(gpt2.GPT2Error) as e:
+        m.backward()
+    assert e.value.code == gpt2.GPT2_ESTATE
+    bad = x.copy()
+    bad[1, 3] = w.V                   # a padded column is not a token
+    with pytest.raises(gpt2.GPT2Error) as e:
+        m.forward(torch.from_numpy(bad).cuda(), torch.from_numpy(y).cuda())
+    assert e.value.code == gpt2.GPT2_ETOKEN
+    # the flag is cleared: a valid step afterwards succeeds
+    loss = m.forward(torch.from_numpy(x).cuda(), torch.from_numpy(y).cuda())
+    assert np.isfinite(loss)
+    m.backward()
+    m.update(1e-3, 0.9, 0.999, 1e-8, 0.0, 1)
+    with pytest.raises(gpt2.GPT2Error) as e:
+        m.update(1e-3, 0.9, 0.999, 1e-8, 0.0, 0)
+    assert e.value.code == gpt2.GPT2_EINVAL

@@ -1,0 +1,86 @@
+// Fused classifier: softmax over the real vocabulary, cross-entropy loss and
+// dLoss/dlogits in one kernel per row, written over the logits in place
+// (the fused cross-entropy of page "llm.c: Large Language Model Training in
+// Pure C/CUDA Without Dependencies"). Padded columns v >= V take no part in
+// the softmax and get a zero gradient.
+#include "kernels.h"
+
+#define CL_THREADS 512
+
+// One block per row: pass 1 keeps a per-thread running (max, sum of exp)
+// over 8-column chunks, merged across the block; pass 2 writes
+// dz = (exp(z - lse) - [v == target]) * dloss.
+template <typename T>
+__global__ __launch_bounds__(CL_THREADS) void classifier_kernel(T* logits,
+                                                                float* __restrict__ losses,
+                                                                const int32_t* __restrict__ targets,
+                                                                int V, int Vp, float dloss,
+                                                                int* err) {
+    __shared__ float red[16];
+    const int64_t row = blockIdx.x;
+    T* z = logits + row * Vp;
+    const int tgt = targets[row];
+    const bool ok = tgt >= 0 && tgt < V;
+    float m = -INFINITY, s = 0.f;
+    for (int c = threadIdx.x * 8; c < V; c += CL_THREADS * 8) {
+        float v[8];
+        load8(z + c, v);
+        float cm = m;
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+            if (c + i < V) cm = fmaxf(cm, v[i]);
+        s *= expf(m - cm);
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+            if (c + i < V) s += expf(v[i] - cm);
+        m = cm;
+    }
+    const float M = block_max(m, red);
+    const float S = block_sum(m == -INFINITY ? 0.f : s * expf(m - M), red);
+    const float lse = M + logf(S);
+    if (threadIdx.x == 0) {
+        if (ok) {
+            losses[row] = lse - to_f32(z[tgt]);
+        } else {
+            losses[row] = 0.f;
+            atomicOr(err, 1);
+        }
+    }
+    __syncthreads();  // the target logit is read before any thread overwrites it
+    for (int c = threadIdx.x * 8; c < Vp; c += CL_THREADS * 8) {
+        float v[8];
+        load8(z + c, v);
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const int col = c + i;
+            float d = 0.f;
+            if (col < V) d = (expf(v[i] - lse) - (col == tgt ? 1.f : 0.f)) * dloss;
+            v[i] = d;
+        }
+        store8(z + c, v);
+    }
+}
+
+template <typename T>
+void classifier_fwd(T* logits, float* losses, const int32_t* targets, int N, int V, int Vp,
+                    float dloss, int* err, hipStream_t st) {
+    classifier_kernel<T><<<N, CL_THREADS, 0, st>>>(logits, losses, targets, V, Vp, dloss, err);
+}
+
+__global__ __launch_bounds__(1024) void loss_mean_kernel(float* out, const float* __restrict__ l,
+                                                         int n) {
+    __shared__ float red[16];
+    float s = 0.f;
+    for (int i = threadIdx.x; i < n; i += blockDim.x) s += l[i];
+    s = block_sum(s, red);
+    if (threadIdx.x == 0) out[0] = s / n;
+}
+
+void loss_mean(float* out, const float* losses, int n, hipStream_t st) {
+    loss_mean_kernel<<<1, 1024, 0, st>>>(out, losses, n);
+}
+
+template void classifier_fwd<float>(float*, float*, const int32_t*, int, int, int, float, int*,
+                                    hipStream_t);
+template void classifier_fwd<bf16>(bf16*, float*, const int32_t*, int, int, int, float, int*,
+                                   hipStream_t);

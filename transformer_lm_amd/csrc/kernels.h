@@ -1,0 +1,81 @@
+// Host-side launchers of the gfx950 kernels. Each enqueues its kernel(s) on
+// `st` and returns immediately. T is the activation storage type (float or
+// bf16); all arithmetic is fp32. Shapes are validated by the caller (gpt2.hip).
+#pragma once
+
+#include "common.h"
+
+// ---- encoder (token + position embedding) ---------------------------------
+// out[b,t,:] = wte[tok[b,t],:] + wpe[t,:]; ids outside [0,V) set *err and
+// produce a zero row.
+template <typename T>
+void encoder_fwd(T* out, const int32_t* tok, const T* wte, const T* wpe, int B, int Tn, int C,
+                 int V, int* err, hipStream_t st);
+// dwte[tok[b,t],:] += dout[b,t,:] (deterministic: positions of one token are
+// summed in increasing order); dwpe[t,:] = sum_b dout[b,t,:], rows >= Tn = 0.
+// ws_*: int32 workspaces of Vp, Vp, Vp+1 and B*Tn elements.
+template <typename T>
+void encoder_bwd(float* dwte, float* dwpe, const T* dout, const int32_t* tok, int B, int Tn,
+                 int C, int Vp, int maxT, int* ws_count, int* ws_cursor, int* ws_offset,
+                 int* ws_bucket, hipStream_t st);
+
+// ---- LayerNorm --------------------------------------------------------------
+template <typename T>
+void layernorm_fwd(T* out, float* mean, float* rstd, const T* inp, const T* w, const T* b,
+                   int N, int C, hipStream_t st);
+// dinp (+)= dx (accumulate != 0 adds); dw, db are written (fp32).
+// partials: fp32 workspace of layernorm_bwd_partials(C) floats.
+template <typename T>
+void layernorm_bwd(T* dinp, int accumulate, float* dw, float* db, const T* dout, const T* inp,
+                   const T* w, const float* mean, const float* rstd, int N, int C,
+                   float* partials, hipStream_t st);
+int64_t layernorm_bwd_partials(int C);
+
+// ---- matmul -----------------------------------------------------------------
+// out[M,N] = inp[M,K] . w[N,K]^T (+ bias[N]) (+ residual[M,N])
+template <typename T>
+void matmul_fwd(T* out, const T* inp, const T* w, const T* bias, const T* residual, int M,
+                int K, int N, hipStream_t st);
+// dinp[M,K] = dout[M,N] . w[N,K]
+template <typename T>
+void matmul_bwd_dx(T* dinp, const T* dout, const T* w, int M, int N, int K, hipStream_t st);
+// dw[N,K] = dout[M,N]^T . inp[M,K] (fp32, written)
+template <typename T>
+void matmul_bwd_dw(float* dw, const T* dout, const T* inp, int M, int N, int K, hipStream_t st);
+// db[N] = sum_m dout[m,:] (fp32, written); partials: bias_bwd_partials(M, N) floats
+template <typename T>
+void bias_bwd(float* db, const T* dout, int M, int N, float* partials, hipStream_t st);
+int64_t bias_bwd_partials(int M, int N);
+
+// ---- attention ---------------------------------------------------------------
+// Causal multi-head attention on qkv (B,T,3C): out (B,T,C), lse (B,NH,T).
+template <typename T>
+void attention_fwd(T* out, float* lse, const T* qkv, int B, int Tn, int C, int NH,
+                   hipStream_t st);
+// dqkv (B,T,3C) written; Dbuf: fp32 workspace (B,NH,T).
+template <typename T>
+void attention_bwd(T* dqkv, const T* dout, const T* qkv, const T* out, const float* lse,
+                   float* Dbuf, int B, int Tn, int C, int NH, hipStream_t st);
+
+// ---- elementwise --------------------------------------------------------------
+template <typename T>
+void gelu_fwd(T* out, const T* inp, int64_t n, hipStream_t st);
+// dinp = gelu'(inp) * dout (written; dinp may alias dout)
+template <typename T>
+void gelu_bwd(T* dinp, const T* inp, const T* dout, int64_t n, hipStream_t st);
+void fill_zero_f32(float* p, int64_t n, hipStream_t st);
+void fill_zero_i32(int* p, int64_t n, hipStream_t st);
+void round_to_bf16(bf16* out, const float* in, int64_t n, hipStream_t st);
+
+// ---- classifier ----------------------------------------------------------------
+// Per row n: lse over the V real columns, losses[n] = lse - z[target];
+// logits overwritten by dz = (softmax - onehot) * dloss (0 on padded columns).
+template <typename T>
+void classifier_fwd(T* logits, float* losses, const int32_t* targets, int N, int V, int Vp,
+                    float dloss, int* err, hipStream_t st);
+// *out = mean of losses[0..n) (fixed summation order)
+void loss_mean(float* out, const float* losses, int n, hipStream_t st);
+
+// ---- AdamW ------------------------------------------------------------------
+void adamw(float* theta, const float* g, float* m, float* v, bf16* theta_bf16, int64_t n,
+           float lr, float b1, float b2, float eps, float wd, float c1, float c2, hipStream_t st);

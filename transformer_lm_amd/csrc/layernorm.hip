@@ -1,0 +1,193 @@
+// LayerNorm forward and backward over rows of C channels (C % 8 == 0,
+// C <= 2048). One wave64 per row; a lane holds up to 4 chunks of 8 channels
+// (chunk k of lane l covers channels (l + 64k) * 8 .. +7) in registers, so a
+// row is read from HBM once. Statistics and all sums are fp32.
+#include "kernels.h"
+
+#define LN_EPS 1e-5f
+#define LN_CHUNKS 4
+#define LN_ROWS_PER_BLOCK 4
+
+// mu = mean(x); var = mean((x - mu)^2) (biased); r = 1/sqrt(var + eps);
+// y = (x - mu) r w + b. Saves mu and r.
+template <typename T>
+__global__ __launch_bounds__(256) void layernorm_fwd_kernel(T* __restrict__ out,
+                                                            float* __restrict__ mean,
+                                                            float* __restrict__ rstd,
+                                                            const T* __restrict__ inp,
+                                                            const T* __restrict__ w,
+                                                            const T* __restrict__ b, int N,
+                                                            int C) {
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * LN_ROWS_PER_BLOCK + (threadIdx.x >> 6);
+    if (row >= N) return;
+    const T* x = inp + (int64_t)row * C;
+    float v[LN_CHUNKS][8];
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < LN_CHUNKS; k++) {
+        int c = (lane + 64 * k) * 8;
+        if (c < C) {
+            load8(x + c, v[k]);
+#pragma unroll
+            for (int i = 0; i < 8; i++) s += v[k][i];
+        }
+    }
+    const float mu = wave_sum(s) / C;
+    float ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < LN_CHUNKS; k++) {
+        int c = (lane + 64 * k) * 8;
+        if (c < C)
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                float d = v[k][i] - mu;
+                ss += d * d;
+            }
+    }
+    const float r = 1.f / sqrtf(wave_sum(ss) / C + LN_EPS);
+#pragma unroll
+    for (int k = 0; k < LN_CHUNKS; k++) {
+        int c = (lane + 64 * k) * 8;
+        if (c < C) {
+            float wv[8], bv[8], o[8];
+            load8(w + c, wv);
+            load8(b + c, bv);
+#pragma unroll
+            for (int i = 0; i < 8; i++) o[i] = (v[k][i] - mu) * r * wv[i] + bv[i];
+            store8(out + (int64_t)row * C + c, o);
+        }
+    }
+    if (lane == 0) {
+        mean[row] = mu;
+        rstd[row] = r;
+    }
+}
+
+template <typename T>
+void layernorm_fwd(T* out, float* mean, float* rstd, const T* inp, const T* w, const T* b,
+                   int N, int C, hipStream_t st) {
+    layernorm_fwd_kernel<T><<<ceil_div(N, LN_ROWS_PER_BLOCK), 256, 0, st>>>(out, mean, rstd, inp,
+                                                                           w, b, N, C);
+}
+
+// Backward. With xhat = (x - mu) r and g = w dy:
+//   dx = r (g - mean(g) - xhat mean(g xhat))
+// dw = sum_rows dy xhat and db = sum_rows dy are reduced deterministically:
+// each block walks a fixed set of rows, its four waves' register sums are
+// combined in wave order through LDS into one partial row per block, and a
+// second kernel sums the partial rows in block order.
+#define LN_BWD_BLOCKS 256
+
+template <typename T>
+__global__ __launch_bounds__(256) void layernorm_bwd_kernel(
+    T* dinp, int accumulate, const T* __restrict__ dout, const T* __restrict__ inp,
+    const T* __restrict__ w, const float* __restrict__ mean, const float* __restrict__ rstd,
+    int N, int C, float* __restrict__ partials) {
+    __shared__ float red[2 * 2048];
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    float dw[LN_CHUNKS][8], db[LN_CHUNKS][8], wv[LN_CHUNKS][8];
+#pragma unroll
+    for (int k = 0; k < LN_CHUNKS; k++) {
+        int c = (lane + 64 * k) * 8;
+#pragma unroll
+        for (int i = 0; i < 8; i++) dw[k][i] = db[k][i] = 0.f;
+        if (c < C) load8(w + c, wv[k]);
+    }
+    for (int row = blockIdx.x * LN_ROWS_PER_BLOCK + wid; row < N;
+         row += gridDim.x * LN_ROWS_PER_BLOCK) {
+        const float mu = mean[row], r = rstd[row];
+        float xh[LN_CHUNKS][8], dy[LN_CHUNKS][8];
+        float gs = 0.f, gxs = 0.f;
+#pragma unroll
+        for (int k = 0; k < LN_CHUNKS; k++) {
+            int c = (lane + 64 * k) * 8;
+            if (c < C) {
+                load8(inp + (int64_t)row * C + c, xh[k]);
+                load8(dout + (int64_t)row * C + c, dy[k]);
+#pragma unroll
+                for (int i = 0; i < 8; i++) {
+                    xh[k][i] = (xh[k][i] - mu) * r;
+                    float g = wv[k][i] * dy[k][i];
+                    gs += g;
+                    gxs += g * xh[k][i];
+                    dw[k][i] += dy[k][i] * xh[k][i];
+                    db[k][i] += dy[k][i];
+                }
+            }
+        }
+        const float gm = wave_sum(gs) / C, gxm = wave_sum(gxs) / C;
+#pragma unroll
+        for (int k = 0; k < LN_CHUNKS; k++) {
+            int c = (lane + 64 * k) * 8;
+            if (c < C) {
+                float o[8];
+                if (accumulate) load8(dinp + (int64_t)row * C + c, o);
+#pragma unroll
+                for (int i = 0; i < 8; i++) {
+                    float dx = (wv[k][i] * dy[k][i] - gm - xh[k][i] * gxm) * r;
+                    o[i] = accumulate ? o[i] + dx : dx;
+                }
+                store8(dinp + (int64_t)row * C + c, o);
+            }
+        }
+    }
+    // combine the four waves in order: wave 0 stores, waves 1..3 add in turn
+    for (int q = 0; q < LN_ROWS_PER_BLOCK; q++) {
+        if (wid == q) {
+#pragma unroll
+            for (int k = 0; k < LN_CHUNKS; k++) {
+                int c = (lane + 64 * k) * 8;
+                if (c < C)
+#pragma unroll
+                    for (int i = 0; i < 8; i++) {
+                        red[c + i] = q == 0 ? dw[k][i] : red[c + i] + dw[k][i];
+                        red[2048 + c + i] = q == 0 ? db[k][i] : red[2048 + c + i] + db[k][i];
+                    }
+            }
+        }
+        __syncthreads();
+    }
+    float* prow = partials + (int64_t)blockIdx.x * 2 * C;
+    for (int c = threadIdx.x; c < C; c += blockDim.x) {
+        prow[c] = red[c];
+        prow[C + c] = red[2048 + c];
+    }
+}
+
+__global__ __launch_bounds__(256) void layernorm_bwd_reduce_kernel(
+    float* __restrict__ dw, float* __restrict__ db, const float* __restrict__ partials,
+    int nblocks, int C) {
+    int j = blockIdx.x * blockDim.x + threadIdx.x;
+    if (j >= 2 * C) return;
+    float s = 0.f;
+    for (int b = 0; b < nblocks; b++) s += partials[(int64_t)b * 2 * C + j];
+    if (j < C)
+        dw[j] = s;
+    else
+        db[j - C] = s;
+}
+
+int64_t layernorm_bwd_partials(int C) { return (int64_t)LN_BWD_BLOCKS * 2 * C; }
+
+template <typename T>
+void layernorm_bwd(T* dinp, int accumulate, float* dw, float* db, const T* dout, const T* inp,
+                   const T* w, const float* mean, const float* rstd, int N, int C,
+                   float* partials, hipStream_t st) {
+    int nb = ceil_div(N, LN_ROWS_PER_BLOCK);
+    if (nb > LN_BWD_BLOCKS) nb = LN_BWD_BLOCKS;
+    layernorm_bwd_kernel<T><<<nb, 256, 0, st>>>(dinp, accumulate, dout, inp, w, mean, rstd, N, C,
+                                                partials);
+    layernorm_bwd_reduce_kernel<<<ceil_div(2 * C, 256), 256, 0, st>>>(dw, db, partials, nb, C);
+}
+
+template void layernorm_fwd<float>(float*, float*, float*, const float*, const float*,
+                                   const float*, int, int, hipStream_t);
+template void layernorm_fwd<bf16>(bf16*, float*, float*, const bf16*, const bf16*, const bf16*,
+                                  int, int, hipStream_t);
+template void layernorm_bwd<float>(float*, int, float*, float*, const float*, const float*,
+                                   const float*, const float*, const float*, int, int, float*,
+                                   hipStream_t);
+template void layernorm_bwd<bf16>(bf16*, int, float*, float*, const bf16*, const bf16*,
+                                  const bf16*, const float*, const float*, int, int, float*,
+                                  hipStream_t);

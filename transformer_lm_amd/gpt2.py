@@ -1,0 +1,238 @@
+"""Python binding of libgpt2.so (include/gpt2.h): the same entry points, with
+argument marshalling only. Every step of the computation runs in the HIP
+kernels behind the C ABI; PyTorch provides device memory and the stream.
+
+Importing this module loads the native library and raises ImportError when it
+is missing: there is no fallback implementation.
+"""
+import ctypes as ct
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgpt2.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run transformer_lm_amd.build.build() "
+                      "(hipcc for gfx950) first")
+
+_lib = ct.CDLL(LIB_PATH)
+
+GPT2_OK, GPT2_EINVAL, GPT2_ESHAPE, GPT2_EHIP, GPT2_ESTATE, GPT2_ETOKEN = 0, -1, -2, -3, -4, -5
+DTYPE_FP32, DTYPE_BF16 = 0, 1
+REGION_MASTER, REGION_GRAD, REGION_M, REGION_V, REGION_PARAM_BF16 = 0, 1, 2, 3, 4
+EXPORTS = ("gpt2_num_params", "gpt2_num_param_tensors", "gpt2_param_table",
+           "gpt2_param_buffer_bytes", "gpt2_act_buffer_bytes", "gpt2_create", "gpt2_forward",
+           "gpt2_backward", "gpt2_update", "gpt2_region", "gpt2_act", "gpt2_free",
+           "gpt2_last_error", "gpt2_timing_arm", "gpt2_timing_classes", "gpt2_timing_read")
+
+
+class Config(ct.Structure):
+    _fields_ = [(n, ct.c_int32) for n in ("V", "Vp", "max_T", "C", "L", "NH", "B", "T", "dtype")]
+
+
+_P = ct.c_void_p
+_CP = ct.POINTER(Config)
+_SIG = {
+    "gpt2_num_params": (ct.c_int64, [_CP]),
+    "gpt2_num_param_tensors": (ct.c_int, []),
+    "gpt2_param_table": (ct.c_int, [_CP, ct.c_int, ct.POINTER(ct.c_char_p),
+                                    ct.POINTER(ct.c_int64), ct.POINTER(ct.c_int32),
+                                    ct.POINTER(ct.c_int32)]),
+    "gpt2_param_buffer_bytes": (ct.c_int64, [_CP]),
+    "gpt2_act_buffer_bytes": (ct.c_int64, [_CP]),
+    "gpt2_create": (ct.c_int, [_CP, _P, _P, ct.POINTER(ct.c_float), _P, ct.POINTER(_P)]),
+    "gpt2_forward": (ct.c_int, [_P, _P, _P, ct.POINTER(ct.c_float)]),
+    "gpt2_backward": (ct.c_int, [_P]),
+    "gpt2_update": (ct.c_int, [_P, ct.c_float, ct.c_float, ct.c_float, ct.c_float, ct.c_float,
+                               ct.c_int32]),
+    "gpt2_region": (ct.c_int, [_P, ct.c_int, ct.POINTER(_P)]),
+    "gpt2_act": (ct.c_int, [_P, ct.c_char_p, ct.POINTER(_P), ct.POINTER(ct.c_int64)]),
+    "gpt2_free": (None, [_P]),
+    "gpt2_last_error": (ct.c_char_p, []),
+    "gpt2_timing_arm": (ct.c_int, [_P, ct.c_char_p, ct.c_int32]),
+    "gpt2_timing_classes": (ct.c_int, []),
+    "gpt2_timing_read": (ct.c_int, [_P, ct.c_int, ct.POINTER(ct.c_char_p),
+                                    ct.POINTER(ct.c_int64), ct.POINTER(ct.c_double),
+                                    ct.POINTER(ct.c_double), ct.POINTER(ct.c_int32)]),
+}
+for _name, (_res, _args) in _SIG.items():
+    _f = getattr(_lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+
+class GPT2Error(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"[{code}] {msg}")
+        self.code = code
+
+
+def last_error():
+    return _lib.gpt2_last_error().decode()
+
+
+def _check(rc):
+    if rc != GPT2_OK:
+        raise GPT2Error(rc, last_error())
+    return rc
+
+
+def config(w):
+    """Config struct for a Workload (transformer_lm_amd.workloads)."""
+    return Config(w.V, w.Vp, w.max_T, w.C, w.L, w.NH, w.B, w.T,
+                  DTYPE_BF16 if w.dtype == "bf16" else DTYPE_FP32)
+
+
+def num_params(cfg):
+    n = _lib.gpt2_num_params(ct.byref(cfg))
+    if n < 0:
+        raise GPT2Error(GPT2_ESHAPE, last_error())
+    return n
+
+
+def param_table(cfg):
+    """[(name, offset, shape)] in storage order."""
+    out = []
+    for i in range(_lib.gpt2_num_param_tensors()):
+        name = ct.c_char_p()
+        off = ct.c_int64()
+        nd = ct.c_int32()
+        shape = (ct.c_int32 * 3)()
+        _check(_lib.gpt2_param_table(ct.byref(cfg), i, ct.byref(name), ct.byref(off),
+                                     ct.byref(nd), shape))
+        out.append((name.value.decode(), off.value, tuple(shape[:nd.value])))
+    return out
+
+
+def param_buffer_bytes(cfg):
+    n = _lib.gpt2_param_buffer_bytes(ct.byref(cfg))
+    if n < 0:
+        raise GPT2Error(GPT2_ESHAPE, last_error())
+    return n
+
+
+def act_buffer_bytes(cfg):
+    n = _lib.gpt2_act_buffer_bytes(ct.byref(cfg))
+    if n < 0:
+        raise GPT2Error(GPT2_ESHAPE, last_error())
+    return n
+
+
+_F32_ACTS = {"ln1_mean", "ln1_rstd", "ln2_mean", "ln2_rstd", "lnf_mean", "lnf_rstd", "att_lse",
+             "losses", "loss", "att_d", "ln_partials", "bias_partials"}
+_I32_ACTS = {"err", "enc_count", "enc_cursor", "enc_offset", "enc_bucket"}
+
+
+class GPT2:
+    """One handle over torch-allocated device buffers on the current stream.
+
+    params: N fp32 initial parameters (numpy or CPU tensor), uploaded by
+    gpt2_create. The torch module is imported lazily (device memory only)."""
+
+    def __init__(self, cfg, params, device="cuda", stream=None):
+        import torch
+        self.torch = torch
+        self.cfg = cfg
+        self.n = num_params(cfg)
+        self.bf16 = cfg.dtype == DTYPE_BF16
+        self.device = torch.device(device)
+        self.stream = stream if stream is not None else torch.cuda.current_stream(self.device)
+        self.pbuf = torch.empty(param_buffer_bytes(cfg), dtype=torch.uint8, device=self.device)
+        self.abuf = torch.empty(act_buffer_bytes(cfg), dtype=torch.uint8, device=self.device)
+        p = np.ascontiguousarray(np.asarray(params, dtype=np.float32).reshape(-1))
+        if p.size != self.n:
+            raise ValueError(f"expected {self.n} parameters, got {p.size}")
+        h = _P()
+        _check(_lib.gpt2_create(ct.byref(cfg), self.pbuf.data_ptr(), self.abuf.data_ptr(),
+                                p.ctypes.data_as(ct.POINTER(ct.c_float)),
+                                self.stream.cuda_stream, ct.byref(h)))
+        self.h = h
+        self._tokens = None
+
+    def close(self):
+        if getattr(self, "h", None):
+            _lib.gpt2_free(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # -- the step ------------------------------------------------------------
+    def forward(self, inputs, targets=None, want_loss=True):
+        """inputs/targets: int32 device tensors (B, T). Returns the mean loss
+        (synchronising) when targets are given and want_loss."""
+        for t in (inputs, targets):
+            if t is not None:
+                assert t.dtype == self.torch.int32 and t.is_contiguous() and t.is_cuda
+                assert t.numel() == self.cfg.B * self.cfg.T
+        self._tokens = (inputs, targets)  # the backward reads the inputs again
+        loss = ct.c_float(float("nan"))
+        lp = ct.byref(loss) if (targets is not None and want_loss) else None
+        _check(_lib.gpt2_forward(self.h, inputs.data_ptr(),
+                                 targets.data_ptr() if targets is not None else None, lp))
+        return loss.value if lp is not None else None
+
+    def backward(self):
+        _check(_lib.gpt2_backward(self.h))
+
+    def update(self, lr, beta1, beta2, eps, weight_decay, step):
+        _check(_lib.gpt2_update(self.h, lr, beta1, beta2, eps, weight_decay, int(step)))
+
+    # -- views ---------------------------------------------------------------
+    def _view(self, buf, ptr, nbytes, dtype):
+        off = ptr - buf.data_ptr()
+        return buf[off:off + nbytes].view(dtype)
+
+    def region(self, which):
+        """Device tensor view of a parameter-buffer region (N elements)."""
+        torch = self.torch
+        p = _P()
+        _check(_lib.gpt2_region(self.h, which, ct.byref(p)))
+        if which == REGION_PARAM_BF16:
+            return self._view(self.pbuf, p.value, self.n * 2, torch.bfloat16)
+        return self._view(self.pbuf, p.value, self.n * 4, torch.float32)
+
+    def act(self, name):
+        """Device tensor view of a named activation (flat)."""
+        torch = self.torch
+        p = _P()
+        nb = ct.c_int64()
+        _check(_lib.gpt2_act(self.h, name.encode(), ct.byref(p), ct.byref(nb)))
+        if name in _F32_ACTS:
+            dt = torch.float32
+        elif name in _I32_ACTS:
+            dt = torch.int32
+        else:
+            dt = torch.bfloat16 if self.bf16 else torch.float32
+        es = torch.tensor([], dtype=dt).element_size()
+        return self._view(self.abuf, p.value, (nb.value // es) * es, dt)
+
+    def synchronize(self):
+        self.stream.synchronize()
+
+    # -- kernel timing ---------------------------------------------------------
+    def timing_arm(self, prefix="", max_launches=4096):
+        """Bracket launches of kernel classes starting with `prefix` with HIP
+        events (None disarms)."""
+        _check(_lib.gpt2_timing_arm(self.h, None if prefix is None else prefix.encode(),
+                                    int(max_launches)))
+
+    def timing_read(self):
+        """{class: (launches, total_ms, work, work_is_bytes)} for recorded classes."""
+        out = {}
+        for i in range(_lib.gpt2_timing_classes()):
+            name = ct.c_char_p()
+            n = ct.c_int64()
+            ms = ct.c_double()
+            wk = ct.c_double()
+            isb = ct.c_int32()
+            _check(_lib.gpt2_timing_read(self.h, i, ct.byref(name), ct.byref(n), ct.byref(ms),
+                                         ct.byref(wk), ct.byref(isb)))
+            if n.value:
+                out[name.value.decode()] = (n.value, ms.value, wk.value, bool(isb.value))
+        return out
