@@ -7,6 +7,8 @@
 // multiple of 8 up to 128, in both storage types. Softmax is computed online
 // over chunks of 64 keys (one key per lane): the running maximum and sum are
 // rescaled chunk by chunk, so the T x T matrix never exists in memory.
+#include <type_traits>
+
 #include "kernels.h"
 
 #define AT_ROWS 4  // rows (waves) per block
@@ -191,9 +193,17 @@ __global__ __launch_bounds__(256) void attention_bwd_dkv_kernel(
     }
 }
 
+// bf16 with head size 64 runs on the matrix cores (attention_mfma.hip); other
+// head sizes and fp32 use the wave-per-row kernels above.
 template <typename T>
 void attention_fwd(T* out, float* lse, const T* qkv, int B, int Tn, int C, int NH,
                    hipStream_t st) {
+    if constexpr (std::is_same<T, bf16>::value) {
+        if (C / NH == 64) {
+            flash_attention_fwd(out, lse, qkv, B, Tn, C, NH, st);
+            return;
+        }
+    }
     dim3 grid(ceil_div(Tn, AT_ROWS), B * NH);
     attention_fwd_rows_kernel<T><<<grid, 256, 0, st>>>(out, lse, qkv, Tn, C, NH);
 }
@@ -203,6 +213,12 @@ void attention_bwd(T* dqkv, const T* dout, const T* qkv, const T* out, const flo
                    float* Dbuf, int B, int Tn, int C, int NH, hipStream_t st) {
     dim3 grid(ceil_div(Tn, AT_ROWS), B * NH);
     attention_bwd_d_kernel<T><<<grid, 256, 0, st>>>(Dbuf, dout, out, Tn, C, NH);
+    if constexpr (std::is_same<T, bf16>::value) {
+        if (C / NH == 64) {
+            flash_attention_bwd(dqkv, dout, qkv, lse, Dbuf, B, Tn, C, NH, st);
+            return;
+        }
+    }
     attention_bwd_dq_kernel<T><<<grid, 256, 0, st>>>(dqkv, dout, qkv, lse, Dbuf, Tn, C, NH);
     attention_bwd_dkv_kernel<T><<<grid, 256, 0, st>>>(dqkv, dout, qkv, lse, Dbuf, Tn, C, NH);
 }

@@ -42,6 +42,13 @@ void matmul_bwd_dx(T* dinp, const T* dout, const T* w, int M, int N, int K, hipS
 // dw[N,K] = dout[M,N]^T . inp[M,K] (fp32, written)
 template <typename T>
 void matmul_bwd_dw(float* dw, const T* dout, const T* inp, int M, int N, int K, hipStream_t st);
+// the bf16 matrix-core kernels behind the three matmul entry points above
+void gemm_bf16_fwd(bf16* out, const bf16* inp, const bf16* w, const bf16* bias,
+                   const bf16* residual, int M, int K, int N, hipStream_t st);
+void gemm_bf16_bwd_dx(bf16* dinp, const bf16* dout, const bf16* w, int M, int N, int K,
+                      hipStream_t st);
+void gemm_bf16_bwd_dw(float* dw, const bf16* dout, const bf16* inp, int M, int N, int K,
+                      hipStream_t st);
 // db[N] = sum_m dout[m,:] (fp32, written); partials: bias_bwd_partials(M, N) floats
 template <typename T>
 void bias_bwd(float* db, const T* dout, int M, int N, float* partials, hipStream_t st);
@@ -56,6 +63,12 @@ void attention_fwd(T* out, float* lse, const T* qkv, int B, int Tn, int C, int N
 template <typename T>
 void attention_bwd(T* dqkv, const T* dout, const T* qkv, const T* out, const float* lse,
                    float* Dbuf, int B, int Tn, int C, int NH, hipStream_t st);
+
+// the bf16 matrix-core kernels for head size 64 behind the two entry points above
+void flash_attention_fwd(bf16* out, float* lse, const bf16* qkv, int B, int Tn, int C, int NH,
+                         hipStream_t st);
+void flash_attention_bwd(bf16* dqkv, const bf16* dout, const bf16* qkv, const float* lse,
+                         const float* Dbuf, int B, int Tn, int C, int NH, hipStream_t st);
 
 // ---- elementwise --------------------------------------------------------------
 template <typename T>

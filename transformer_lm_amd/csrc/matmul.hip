@@ -5,6 +5,8 @@
 // storage types: out[i, j] = sum_p X(i, p) Y(j, p) with
 // X(i, p) = X[i*sxi + p*sxp] and Y(j, p) = Y[j*syj + p*syp]; 64x64 output tiles,
 // K-steps of 16 staged in LDS, fp32 accumulation, 4x4 outputs per thread.
+#include <type_traits>
+
 #include "kernels.h"
 
 #define GT_M 64
@@ -94,23 +96,35 @@ static void gemm_generic(TO* out, const TX* X, const TY* Y, const TR* bias, cons
                                                               sxi, sxp, syj, syp, ldo);
 }
 
+// bf16 storage runs on the matrix cores (gemm_mfma.hip); fp32 storage uses the
+// general-stride kernel above.
 template <typename T>
 void matmul_fwd(T* out, const T* inp, const T* w, const T* bias, const T* residual, int M,
                 int K, int N, hipStream_t st) {
     // out[m, n] = sum_k inp[m, k] w[n, k]
-    gemm_generic<T, T, T, T>(out, inp, w, bias, residual, M, N, K, K, 1, K, 1, N, st);
+    if constexpr (std::is_same<T, bf16>::value)
+        gemm_bf16_fwd(out, inp, w, bias, residual, M, K, N, st);
+    else
+        gemm_generic<T, T, T, T>(out, inp, w, bias, residual, M, N, K, K, 1, K, 1, N, st);
 }
 
 template <typename T>
 void matmul_bwd_dx(T* dinp, const T* dout, const T* w, int M, int N, int K, hipStream_t st) {
     // dinp[m, k] = sum_n dout[m, n] w[n, k]
-    gemm_generic<T, T, T, T>(dinp, dout, w, nullptr, nullptr, M, K, N, N, 1, 1, K, K, st);
+    if constexpr (std::is_same<T, bf16>::value)
+        gemm_bf16_bwd_dx(dinp, dout, w, M, N, K, st);
+    else
+        gemm_generic<T, T, T, T>(dinp, dout, w, nullptr, nullptr, M, K, N, N, 1, 1, K, K, st);
 }
 
 template <typename T>
 void matmul_bwd_dw(float* dw, const T* dout, const T* inp, int M, int N, int K, hipStream_t st) {
     // dw[n, k] = sum_m dout[m, n] inp[m, k]
-    gemm_generic<T, T, float, float>(dw, dout, inp, nullptr, nullptr, N, K, M, 1, N, 1, K, K, st);
+    if constexpr (std::is_same<T, bf16>::value)
+        gemm_bf16_bwd_dw(dw, dout, inp, M, N, K, st);
+    else
+        gemm_generic<T, T, float, float>(dw, dout, inp, nullptr, nullptr, N, K, M, 1, N, 1, K, K,
+                                         st);
 }
 
 // Bias gradient db[n] = sum_m dout[m, n], deterministic two-stage column sum:
