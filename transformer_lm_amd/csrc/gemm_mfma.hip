@@ -5,10 +5,15 @@
 // row-contiguous (X[p*ld + i]). Every tile is staged into LDS
 // reduction-contiguous, which is what an MFMA fragment wants: lane l reads
 // 8 consecutive reduction elements (16 bytes) of tile row l % 32. A
-// row-contiguous operand is transposed on the way into LDS.
+// row-contiguous operand is transposed on the way into LDS: a thread loads
+// 8 rows x 2 reduction steps (two 16-byte loads) and packs each row's pair
+// into one dword with v_perm_b32 before writing it.
 //   forward  y  = x W^T      X = x  (p-contig), Y = W  (p-contig)
 //   backward dx = dy W       X = dy (p-contig), Y = W  (row-contig)
 //   backward dW = dy^T x     X = dy (row-contig), Y = x (row-contig)
+// The weight gradient reduces over all B*T rows; its few output tiles are
+// split along that reduction (grid z), each split writing an fp32 partial that
+// a second kernel sums in split order (deterministic).
 //
 // The MFMA "row" dimension is the output column j, so each lane's
 // accumulators hold runs of 4 consecutive j and stores are 8-byte (bf16) or
@@ -21,34 +26,42 @@ typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 #define LDS_PAD 8  // bf16 elements of padding per LDS row (spreads rows over banks)
 
 template <int ROWS, int BK, int NT, bool RC>
 struct Stager {
-    // chunks of 8 bf16 per thread per k-tile
-    static constexpr int CH = (ROWS * BK / 8 + NT - 1) / NT;
-    bf16x8 r[CH];
+    // p-contig: one chunk = 8 consecutive p of one row (16 B)
+    // row-contig: one chunk = 8 consecutive rows x 2 consecutive p (2 x 16 B)
+    static constexpr int NCHUNK = RC ? (ROWS / 8) * (BK / 2) : ROWS * BK / 8;
+    static constexpr int CH = (NCHUNK + NT - 1) / NT;
+    static constexpr int NV = RC ? 2 : 1;
+    u32x4 r[CH][NV];
 
-    // Global -> registers for the tile at (row0, k0).
-    __device__ __forceinline__ void load(const bf16* __restrict__ g, int ld, int nrows, int K,
+    // Global -> registers for the tile at (row0, k0); rows >= nrows and
+    // reduction indices >= kend read as zero.
+    __device__ __forceinline__ void load(const bf16* __restrict__ g, int ld, int nrows, int kend,
                                          int row0, int k0, int tid) {
 #pragma unroll
         for (int q = 0; q < CH; q++) {
             const int c = tid + q * NT;
-            bf16x8 v = {};
-            if (c < ROWS * BK / 8) {
-                if (!RC) {  // g[row * ld + p]: chunk = 8 consecutive p of one row
-                    const int row = c / (BK / 8), kc = (c % (BK / 8)) * 8;
-                    if (row0 + row < nrows && k0 + kc < K)
-                        v = *reinterpret_cast<const bf16x8*>(g + (int64_t)(row0 + row) * ld + k0 + kc);
-                } else {    // g[p * ld + row]: chunk = 8 consecutive rows of one p
-                    const int p = c / (ROWS / 8), rc = (c % (ROWS / 8)) * 8;
-                    if (k0 + p < K && row0 + rc < nrows)
-                        v = *reinterpret_cast<const bf16x8*>(g + (int64_t)(k0 + p) * ld + row0 + rc);
-                }
+#pragma unroll
+            for (int u = 0; u < NV; u++) r[q][u] = u32x4{0u, 0u, 0u, 0u};
+            if (c >= NCHUNK) continue;
+            if (!RC) {
+                const int row = c / (BK / 8), kc = (c % (BK / 8)) * 8;
+                if (row0 + row < nrows && k0 + kc < kend)
+                    r[q][0] = *reinterpret_cast<const u32x4*>(g + (int64_t)(row0 + row) * ld + k0 + kc);
+            } else {
+                const int pp = (c % (BK / 2)) * 2, rc = (c / (BK / 2)) * 8;
+                if (row0 + rc < nrows)
+#pragma unroll
+                    for (int u = 0; u < 2; u++)
+                        if (k0 + pp + u < kend)
+                            r[q][u] = *reinterpret_cast<const u32x4*>(
+                                g + (int64_t)(k0 + pp + u) * ld + row0 + rc);
             }
-            r[q] = v;
         }
     }
 
@@ -57,14 +70,19 @@ struct Stager {
 #pragma unroll
         for (int q = 0; q < CH; q++) {
             const int c = tid + q * NT;
-            if (c < ROWS * BK / 8) {
-                if (!RC) {
-                    const int row = c / (BK / 8), kc = (c % (BK / 8)) * 8;
-                    *reinterpret_cast<bf16x8*>(s + row * (BK + LDS_PAD) + kc) = r[q];
-                } else {
-                    const int p = c / (ROWS / 8), rc = (c % (ROWS / 8)) * 8;
+            if (c >= NCHUNK) continue;
+            if (!RC) {
+                const int row = c / (BK / 8), kc = (c % (BK / 8)) * 8;
+                *reinterpret_cast<u32x4*>(s + row * (BK + LDS_PAD) + kc) = r[q][0];
+            } else {
+                const int pp = (c % (BK / 2)) * 2, rc = (c / (BK / 2)) * 8;
+                unsigned int* d = reinterpret_cast<unsigned int*>(s + rc * (BK + LDS_PAD) + pp);
+                constexpr int DW = (BK + LDS_PAD) / 2;  // dwords per LDS row
 #pragma unroll
-                    for (int e = 0; e < 8; e++) s[(rc + e) * (BK + LDS_PAD) + p] = r[q][e];
+                for (int w = 0; w < 4; w++) {
+                    // rows rc+2w (low halves) and rc+2w+1 (high halves): pair (p, p+1)
+                    d[(2 * w) * DW] = __builtin_amdgcn_perm(r[q][1][w], r[q][0][w], 0x05040100u);
+                    d[(2 * w + 1) * DW] = __builtin_amdgcn_perm(r[q][1][w], r[q][0][w], 0x07060302u);
                 }
             }
         }
@@ -78,7 +96,7 @@ template <int BM, int BN, int BK, int WM, int WN, bool XRC, bool YRC, int EPI>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_mfma_kernel(
     void* __restrict__ out_, const bf16* __restrict__ X, const bf16* __restrict__ Y,
     const bf16* __restrict__ bias, const bf16* __restrict__ residual, int M, int N, int K,
-    int ldx, int ldy, int ldo) {
+    int ldx, int ldy, int ldo, int kchunk, int64_t split_stride) {
     constexpr int NT = WM * WN * 64;
     constexpr int TM = BM / WM, TN = BN / WN;  // wave tile (i extent, j extent)
     constexpr int FM = TM / 32, FN = TN / 32;  // 32x32 MFMA tiles per wave
@@ -89,6 +107,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mfma_kernel(
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int wm = wid % WM, wn = wid / WM;
     const int i0 = blockIdx.y * BM, j0 = blockIdx.x * BN;
+    const int kbeg = blockIdx.z * kchunk, kend = min(K, kbeg + kchunk);
 
     Stager<BM, BK, NT, XRC> xs;
     Stager<BN, BK, NT, YRC> ys;
@@ -98,9 +117,9 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mfma_kernel(
 #pragma unroll
         for (int b = 0; b < FM; b++) acc[a][b] = floatx16{};
 
-    const int nk = (K + BK - 1) / BK;
-    xs.load(X, ldx, M, K, i0, 0, tid);
-    ys.load(Y, ldy, N, K, j0, 0, tid);
+    const int nk = (kend - kbeg + BK - 1) / BK;
+    xs.load(X, ldx, M, kend, i0, kbeg, tid);
+    ys.load(Y, ldy, N, kend, j0, kbeg, tid);
     xs.store(Xs[0], tid);
     ys.store(Ys[0], tid);
     __syncthreads();
@@ -109,8 +128,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mfma_kernel(
     for (int kt = 0; kt < nk; kt++) {
         const int buf = kt & 1;
         if (kt + 1 < nk) {
-            xs.load(X, ldx, M, K, i0, (kt + 1) * BK, tid);
-            ys.load(Y, ldy, N, K, j0, (kt + 1) * BK, tid);
+            xs.load(X, ldx, M, kend, i0, kbeg + (kt + 1) * BK, tid);
+            ys.load(Y, ldy, N, kend, j0, kbeg + (kt + 1) * BK, tid);
         }
         const bf16* xb = Xs[buf] + (wm * TM + fr) * LDR + fk;
         const bf16* yb = Ys[buf] + (wn * TN + fr) * LDR + fk;
@@ -149,7 +168,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mfma_kernel(
                 float v0 = acc[fn][fm][4 * g], v1 = acc[fn][fm][4 * g + 1];
                 float v2 = acc[fn][fm][4 * g + 2], v3 = acc[fn][fm][4 * g + 3];
                 if (EPI == EPI_F32) {
-                    float* o = reinterpret_cast<float*>(out_) + (int64_t)i * ldo + j;
+                    float* o = reinterpret_cast<float*>(out_) + blockIdx.z * split_stride +
+                               (int64_t)i * ldo + j;
                     *reinterpret_cast<floatx4*>(o) = floatx4{v0, v1, v2, v3};
                 } else {
                     if (bias) {
@@ -174,30 +194,68 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mfma_kernel(
         }
 }
 
+// out[e] = sum_z part[z * n + e], z in order (n % 4 == 0)
+__global__ __launch_bounds__(256) void split_reduce_kernel(float* __restrict__ out,
+                                                           const float* __restrict__ part,
+                                                           int splits, int64_t n) {
+    const int64_t i = (blockIdx.x * (int64_t)blockDim.x + threadIdx.x) * 4;
+    if (i >= n) return;
+    floatx4 s = *reinterpret_cast<const floatx4*>(part + i);
+    for (int z = 1; z < splits; z++) s += *reinterpret_cast<const floatx4*>(part + z * n + i);
+    *reinterpret_cast<floatx4*>(out + i) = s;
+}
+
+constexpr int GBM = 128, GBN = 128, GBK = 32, GWM = 2, GWN = 2;
+
 template <bool XRC, bool YRC, int EPI>
 static void launch(void* out, const bf16* X, const bf16* Y, const bf16* bias,
                    const bf16* residual, int M, int N, int K, int ldx, int ldy, int ldo,
-                   hipStream_t st) {
-    constexpr int BM = 128, BN = 128, BK = 32, WM = 2, WN = 2;
-    dim3 grid(ceil_div(N, BN), ceil_div(M, BM));
-    gemm_mfma_kernel<BM, BN, BK, WM, WN, XRC, YRC, EPI><<<grid, WM * WN * 64, 0, st>>>(
-        out, X, Y, bias, residual, M, N, K, ldx, ldy, ldo);
+                   int splits, int kchunk, int64_t split_stride, hipStream_t st) {
+    dim3 grid(ceil_div(N, GBN), ceil_div(M, GBM), splits);
+    gemm_mfma_kernel<GBM, GBN, GBK, GWM, GWN, XRC, YRC, EPI><<<grid, GWM * GWN * 64, 0, st>>>(
+        out, X, Y, bias, residual, M, N, K, ldx, ldy, ldo, kchunk, split_stride);
 }
 
 // out[M,N] = inp[M,K] . w[N,K]^T (+ bias) (+ residual)
 void gemm_bf16_fwd(bf16* out, const bf16* inp, const bf16* w, const bf16* bias,
                    const bf16* residual, int M, int K, int N, hipStream_t st) {
-    launch<false, false, EPI_BF16>(out, inp, w, bias, residual, M, N, K, K, K, N, st);
+    launch<false, false, EPI_BF16>(out, inp, w, bias, residual, M, N, K, K, K, N, 1, K, 0, st);
 }
 
 // dinp[M,K] = dout[M,N] . w[N,K]
 void gemm_bf16_bwd_dx(bf16* dinp, const bf16* dout, const bf16* w, int M, int N, int K,
                       hipStream_t st) {
-    launch<false, true, EPI_BF16>(dinp, dout, w, nullptr, nullptr, M, K, N, N, K, K, st);
+    launch<false, true, EPI_BF16>(dinp, dout, w, nullptr, nullptr, M, K, N, N, K, K, 1, N, 0, st);
 }
 
-// dw[N,K] (fp32) = dout[M,N]^T . inp[M,K]
+// Splits of the B*T reduction of a weight gradient [N, K]: enough blocks to
+// cover the chip about four times over, each split at least 512 rows long.
+static int dw_splits(int M, int N, int K) {
+    const int tiles = ceil_div(N, GBM) * ceil_div(K, GBN);
+    int s = (4 * 256 + tiles - 1) / tiles;
+    const int smax = M / 512;
+    if (s > smax) s = smax;
+    if (s > 16) s = 16;
+    return s < 1 ? 1 : s;
+}
+
+int64_t gemm_dw_workspace_floats(int M, int N, int K) {
+    const int s = dw_splits(M, N, K);
+    return s > 1 ? (int64_t)s * N * K : 0;
+}
+
+// dw[N,K] (fp32) = dout[M,N]^T . inp[M,K]; ws: gemm_dw_workspace_floats(M,N,K) floats
 void gemm_bf16_bwd_dw(float* dw, const bf16* dout, const bf16* inp, int M, int N, int K,
-                      hipStream_t st) {
-    launch<true, true, EPI_F32>(dw, dout, inp, nullptr, nullptr, N, K, M, N, K, K, st);
+                      float* ws, hipStream_t st) {
+    const int s = dw_splits(M, N, K);
+    if (s == 1) {
+        launch<true, true, EPI_F32>(dw, dout, inp, nullptr, nullptr, N, K, M, N, K, K, 1, M, 0, st);
+        return;
+    }
+    const int kchunk = ceil_div(ceil_div(M, s), GBK) * GBK;
+    const int splits = ceil_div(M, kchunk);
+    launch<true, true, EPI_F32>(ws, dout, inp, nullptr, nullptr, N, K, M, N, K, K, splits, kchunk,
+                                (int64_t)N * K, st);
+    const int64_t n = (int64_t)N * K;
+    split_reduce_kernel<<<ceil_div(n / 4, 256), 256, 0, st>>>(dw, ws, splits, n);
 }

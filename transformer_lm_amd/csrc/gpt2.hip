@@ -43,7 +43,7 @@ enum {
     A_LN2, A_LN2_MEAN, A_LN2_RSTD, A_FCH, A_FCH_GELU, A_RESIDUAL3, A_LNF, A_LNF_MEAN,
     A_LNF_RSTD, A_LOGITS, A_LOSSES, A_LOSS, A_ERR,
     W_DRES, W_DC, W_D3C, W_D4C, W_ATT_D, W_LN_PART, W_BIAS_PART, W_ENC_COUNT, W_ENC_CURSOR,
-    W_ENC_OFFSET, W_ENC_BUCKET, NUM_A
+    W_ENC_OFFSET, W_ENC_BUCKET, W_DW_SPLIT, NUM_A
 };
 
 const char* const A_NAMES[NUM_A] = {
@@ -51,7 +51,7 @@ const char* const A_NAMES[NUM_A] = {
     "ln2", "ln2_mean", "ln2_rstd", "fch", "fch_gelu", "residual3", "lnf", "lnf_mean",
     "lnf_rstd", "logits", "losses", "loss", "err",
     "dresidual", "dbuf_c", "dbuf_3c", "dbuf_4c", "att_d", "ln_partials", "bias_partials",
-    "enc_count", "enc_cursor", "enc_offset", "enc_bucket"};
+    "enc_count", "enc_cursor", "enc_offset", "enc_bucket", "dw_split"};
 
 constexpr int64_t ALIGN = 256;
 int64_t align_up(int64_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
@@ -142,6 +142,16 @@ void plan(const gpt2_config* c, Layout* lay) {
     a[W_ENC_COUNT] = a[W_ENC_CURSOR] = V * 4;
     a[W_ENC_OFFSET] = (V + 1) * 4;
     a[W_ENC_BUCKET] = BT * 4;
+    // split-reduction partials of the bf16 weight-gradient products
+    int64_t dwf = 0;
+    if (c->dtype == GPT2_DTYPE_BF16) {
+        const int64_t shapes[5][2] = {{3 * C, C}, {C, C}, {4 * C, C}, {C, 4 * C}, {V, C}};
+        for (auto& s : shapes) {
+            const int64_t f = gemm_dw_workspace_floats((int)BT, (int)s[0], (int)s[1]);
+            if (f > dwf) dwf = f;
+        }
+    }
+    a[W_DW_SPLIT] = dwf * 4;
     int64_t o = 0;
     for (int i = 0; i < NUM_A; i++) {
         lay->aoff[i] = o;
@@ -360,6 +370,7 @@ void backward_impl(gpt2* h) {
     float* attD = (float*)h->a[W_ATT_D];
     float* lnp = (float*)h->a[W_LN_PART];
     float* bp = (float*)h->a[W_BIAS_PART];
+    float* dws = (float*)h->a[W_DW_SPLIT];
     // LayerNorm backward reads x and dy, reads+writes (or writes) dx
     auto ln_bytes = [&](bool acc) { return (acc ? 4.0 : 3.0) * nC * es + 8.0 * BT + C * (es + 8); };
     auto bb_bytes = [&](double N) { return BT * N * es + 4.0 * N; };
@@ -372,7 +383,7 @@ void backward_impl(gpt2* h) {
     }
     {
         KScope k(h, K_MATMUL_BWD_DW, mm_flops(Vp, C, BT));
-        matmul_bwd_dw<T>(G[P_WTE], dlogits, lnf, BT, Vp, C, st);
+        matmul_bwd_dw<T>(G[P_WTE], dlogits, lnf, BT, Vp, C, dws, st);
     }
     {
         KScope k(h, K_LAYERNORM_BWD, ln_bytes(false));
@@ -389,7 +400,7 @@ void backward_impl(gpt2* h) {
         }
         {
             KScope k(h, K_MATMUL_BWD_DW, mm_flops(C, 4 * C, BT));
-            matmul_bwd_dw<T>(G[P_FCPROJW] + w4, dres, fchg + l * 4 * nC, BT, C, 4 * C, st);
+            matmul_bwd_dw<T>(G[P_FCPROJW] + w4, dres, fchg + l * 4 * nC, BT, C, 4 * C, dws, st);
         }
         {
             KScope k(h, K_BIAS_BWD, bb_bytes(C));
@@ -405,7 +416,7 @@ void backward_impl(gpt2* h) {
         }
         {
             KScope k(h, K_MATMUL_BWD_DW, mm_flops(4 * C, C, BT));
-            matmul_bwd_dw<T>(G[P_FCW] + w4, d4C, ln2 + l * nC, BT, 4 * C, C, st);
+            matmul_bwd_dw<T>(G[P_FCW] + w4, d4C, ln2 + l * nC, BT, 4 * C, C, dws, st);
         }
         {
             KScope k(h, K_BIAS_BWD, bb_bytes(4 * C));
@@ -425,7 +436,7 @@ void backward_impl(gpt2* h) {
         }
         {
             KScope k(h, K_MATMUL_BWD_DW, mm_flops(C, C, BT));
-            matmul_bwd_dw<T>(G[P_ATTPROJW] + w1, dres, atty + l * nC, BT, C, C, st);
+            matmul_bwd_dw<T>(G[P_ATTPROJW] + w1, dres, atty + l * nC, BT, C, C, dws, st);
         }
         {
             KScope k(h, K_BIAS_BWD, bb_bytes(C));
@@ -442,7 +453,7 @@ void backward_impl(gpt2* h) {
         }
         {
             KScope k(h, K_MATMUL_BWD_DW, mm_flops(3 * C, C, BT));
-            matmul_bwd_dw<T>(G[P_QKVW] + w3, d3C, ln1 + l * nC, BT, 3 * C, C, st);
+            matmul_bwd_dw<T>(G[P_QKVW] + w3, d3C, ln1 + l * nC, BT, 3 * C, C, dws, st);
         }
         {
             KScope k(h, K_BIAS_BWD, bb_bytes(3 * C));

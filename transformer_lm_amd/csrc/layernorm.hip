@@ -77,7 +77,7 @@ void layernorm_fwd(T* out, float* mean, float* rstd, const T* inp, const T* w, c
 // each block walks a fixed set of rows, its four waves' register sums are
 // combined in wave order through LDS into one partial row per block, and a
 // second kernel sums the partial rows in block order.
-#define LN_BWD_BLOCKS 256
+#define LN_BWD_BLOCKS 1024
 
 template <typename T>
 __global__ __launch_bounds__(256) void layernorm_bwd_kernel(
@@ -155,17 +155,25 @@ __global__ __launch_bounds__(256) void layernorm_bwd_kernel(
     }
 }
 
+// 64 partial columns per block, 4 row phases per column combined in order.
 __global__ __launch_bounds__(256) void layernorm_bwd_reduce_kernel(
     float* __restrict__ dw, float* __restrict__ db, const float* __restrict__ partials,
     int nblocks, int C) {
-    int j = blockIdx.x * blockDim.x + threadIdx.x;
-    if (j >= 2 * C) return;
+    __shared__ float red[4][64];
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    const int j = blockIdx.x * 64 + tx;
     float s = 0.f;
-    for (int b = 0; b < nblocks; b++) s += partials[(int64_t)b * 2 * C + j];
-    if (j < C)
-        dw[j] = s;
-    else
-        db[j - C] = s;
+    if (j < 2 * C)
+        for (int b = ty; b < nblocks; b += 4) s += partials[(int64_t)b * 2 * C + j];
+    red[ty][tx] = s;
+    __syncthreads();
+    if (ty == 0 && j < 2 * C) {
+        const float t = ((red[0][tx] + red[1][tx]) + red[2][tx]) + red[3][tx];
+        if (j < C)
+            dw[j] = t;
+        else
+            db[j - C] = t;
+    }
 }
 
 int64_t layernorm_bwd_partials(int C) { return (int64_t)LN_BWD_BLOCKS * 2 * C; }
@@ -178,7 +186,7 @@ void layernorm_bwd(T* dinp, int accumulate, float* dw, float* db, const T* dout,
     if (nb > LN_BWD_BLOCKS) nb = LN_BWD_BLOCKS;
     layernorm_bwd_kernel<T><<<nb, 256, 0, st>>>(dinp, accumulate, dout, inp, w, mean, rstd, N, C,
                                                 partials);
-    layernorm_bwd_reduce_kernel<<<ceil_div(2 * C, 256), 256, 0, st>>>(dw, db, partials, nb, C);
+    layernorm_bwd_reduce_kernel<<<ceil_div(2 * C, 64), 256, 0, st>>>(dw, db, partials, nb, C);
 }
 
 template void layernorm_fwd<float>(float*, float*, float*, const float*, const float*,

@@ -118,30 +118,48 @@ void matmul_bwd_dx(T* dinp, const T* dout, const T* w, int M, int N, int K, hipS
 }
 
 template <typename T>
-void matmul_bwd_dw(float* dw, const T* dout, const T* inp, int M, int N, int K, hipStream_t st) {
+void matmul_bwd_dw(float* dw, const T* dout, const T* inp, int M, int N, int K, float* ws,
+                   hipStream_t st) {
     // dw[n, k] = sum_m dout[m, n] inp[m, k]
     if constexpr (std::is_same<T, bf16>::value)
-        gemm_bf16_bwd_dw(dw, dout, inp, M, N, K, st);
+        gemm_bf16_bwd_dw(dw, dout, inp, M, N, K, ws, st);
     else
         gemm_generic<T, T, float, float>(dw, dout, inp, nullptr, nullptr, N, K, M, 1, N, 1, K, K,
                                          st);
 }
 
-// Bias gradient db[n] = sum_m dout[m, n], deterministic two-stage column sum:
-// stage 1 sums BB_ROWS rows per block into one partial row, stage 2 sums the
-// partial rows in order.
-#define BB_ROWS 256
+// Bias gradient db[n] = sum_m dout[m, n], deterministic two-stage column sum.
+// Stage 1: a block covers 256 columns (32 threads x 8 columns, 16-byte loads)
+// and BB_ROWS rows split over 8 row phases; the phases are combined in order
+// through LDS into one partial row. Stage 2 sums the partial rows in order.
+#define BB_ROWS 128
 
 template <typename T>
 __global__ __launch_bounds__(256) void bias_bwd_partial_kernel(float* __restrict__ partials,
                                                                const T* __restrict__ dout,
                                                                int M, int N) {
-    const int n = blockIdx.x * blockDim.x + threadIdx.x;
-    if (n >= N) return;
+    __shared__ float red[8][256];
+    const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+    const int n = blockIdx.x * 256 + tx * 8;
     const int m0 = blockIdx.y * BB_ROWS, m1 = min(M, m0 + BB_ROWS);
-    float s = 0.f;
-    for (int m = m0; m < m1; m++) s += to_f32(dout[(int64_t)m * N + n]);
-    partials[(int64_t)blockIdx.y * N + n] = s;
+    float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (n < N)
+        for (int m = m0 + ty; m < m1; m += 8) {
+            float v[8];
+            load8(dout + (int64_t)m * N + n, v);
+#pragma unroll
+            for (int k = 0; k < 8; k++) s[k] += v[k];
+        }
+#pragma unroll
+    for (int k = 0; k < 8; k++) red[ty][tx * 8 + k] = s[k];
+    __syncthreads();
+    const int c = threadIdx.x, nc = blockIdx.x * 256 + c;
+    if (nc < N) {
+        float t = 0.f;
+#pragma unroll
+        for (int r = 0; r < 8; r++) t += red[r][c];
+        partials[(int64_t)blockIdx.y * N + nc] = t;
+    }
 }
 
 __global__ __launch_bounds__(256) void bias_bwd_reduce_kernel(float* __restrict__ db,
@@ -168,7 +186,8 @@ void bias_bwd(float* db, const T* dout, int M, int N, float* partials, hipStream
     template void matmul_fwd<T>(T*, const T*, const T*, const T*, const T*, int, int, int,      \
                                 hipStream_t);                                                  \
     template void matmul_bwd_dx<T>(T*, const T*, const T*, int, int, int, hipStream_t);         \
-    template void matmul_bwd_dw<T>(float*, const T*, const T*, int, int, int, hipStream_t);     \
+    template void matmul_bwd_dw<T>(float*, const T*, const T*, int, int, int, float*,          \
+                                   hipStream_t);                                               \
     template void bias_bwd<T>(float*, const T*, int, int, float*, hipStream_t);
 INST(float)
 INST(bf16)
