@@ -148,9 +148,9 @@ int gpt2_act(gpt2* h, const char* name, void** d_ptr, int64_t* bytes);
  * a pair of HIP events on the handle's stream, for up to max_launches
  * launches; arming discards earlier records. Classes: "encoder_fwd",
  * "layernorm_fwd", "matmul_fwd", "attention_fwd", "gelu_fwd", "classifier",
- * "matmul_bwd_dx", "matmul_bwd_dw", "bias_bwd", "gelu_bwd", "layernorm_bwd",
- * "attention_bwd", "encoder_bwd", "adamw". The events are created at arming
- * (no device memory is allocated). */
+ * "matmul_bwd_dx", "matmul_bwd_dw" (weight and bias gradients), "gelu_bwd",
+ * "layernorm_bwd", "attention_bwd", "encoder_bwd", "adamw". The events are
+ * created at arming (no device memory is allocated). */
 int gpt2_timing_arm(gpt2* h, const char* prefix, int32_t max_launches);
 
 /* Per-class totals over the recorded launches; synchronises the stream.

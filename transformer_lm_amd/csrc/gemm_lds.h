@@ -1,0 +1,268 @@
+// bf16 matrix products fed by direct global -> LDS loads (gfx950
+// global_load_lds_dwordx4), for the three operand layouts of the linear
+// layers, on v_mfma_f32_32x32x16_bf16 with fp32 accumulation:
+//   out[i, j] = sum_p X(i, p) Y(j, p) (+ bias[j]) (+ residual[i, j]).
+//
+// Each load instruction of a wave writes 64 x 16 bytes to consecutive LDS
+// addresses in lane order, so a tile keeps the layout it has in global memory:
+//   reduction-contiguous operand (X[i*ld + p]):  LDS [rows][BK]
+//   row-contiguous operand       (X[p*ld + i]):  LDS [BK][rows]
+// Which global 16-byte chunk a lane fetches is XOR-permuted within its LDS
+// row, so that fragment reads hit distinct banks. MFMA fragments (lane l:
+// tile row l%32, 8 consecutive reduction indices 8*(l/32)..+7) come from a
+// reduction-contiguous tile with one ds_read_b128, and from a row-contiguous
+// tile with two ds_read_b64_tr_b16: that transpose read gives lane o of a
+// 16-lane group column c0+o of rows k0..k0+3 when lane i of the group points
+// at row k0 + i/4, columns c0 + 4*(i%4).
+//
+// Tiles sit in an S-stage LDS ring: stage k+S-1 is requested before stage k
+// is computed, so the loads of S-1 stages are in flight while the matrix cores
+// work, and no registers hold staged data. Waits count only the stages that
+// must have landed (s_waitcnt vmcnt(N)); a plain s_barrier then publishes them
+// (a __syncthreads() would also drain the later stages' loads).
+//
+// Requirements: the reduction length is a multiple of BK (each split's too);
+// row counts of row-contiguous operands are multiples of 8. Rows past the
+// matrix edge are fetched from clamped addresses and their outputs discarded.
+#pragma once
+
+#include "gemm_mfma.h"
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+// chunk permutation of a reduction-contiguous LDS row r (BK elements)
+template <int BK>
+__device__ __forceinline__ int pc_swz(int r) {
+    if constexpr (BK == 64) return (r & 7) ^ ((r >> 3) & 1);
+    else return (r >> 2) & 3;  // BK == 32
+}
+
+// chunk permutation of a row-contiguous LDS row k (ROWS elements): even
+// values, so the 32-byte runs read by the transpose loads stay whole
+template <int ROWS>
+__device__ __forceinline__ int rc_swz(int k) {
+    if constexpr ((ROWS * 2) % 256 == 0) return 2 * (k & 3);
+    else return 2 * ((k >> 1) & 1);  // rows 128 bytes off a 256-byte bank line
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// One operand tile (ROWS x BK) of the ring: its loads and fragment reads.
+template <int ROWS, int BK, int NW, bool RC>
+struct LdsOperand {
+    static constexpr int CHUNKS = ROWS * BK / 8;  // 16-byte chunks per tile
+    static constexpr int TOTAL = CHUNKS / 64;     // wave load instructions per tile
+    static constexpr int NPW = (TOTAL + NW - 1) / NW;
+    static constexpr int ELEMS = ROWS * BK;
+    static_assert(TOTAL * 64 == CHUNKS, "a tile is a whole number of wave loads");
+
+    // Loads the tile at rows row0.., reduction k0.. into LDS at s. The last
+    // wave may repeat its final chunk so that all waves issue NPW loads.
+    __device__ __forceinline__ static void load(bf16* s, const bf16* __restrict__ g, int ld,
+                                                int nrows, int row0, int k0, int wid, int lane) {
+#pragma unroll
+        for (int j = 0; j < NPW; j++) {
+            const int blk = min(wid * NPW + j, TOTAL - 1);
+            const int ch = blk * 64 + lane;
+            const bf16* src;
+            if (!RC) {
+                constexpr int CPR = BK / 8;
+                const int r = ch / CPR, lc = (ch % CPR) ^ pc_swz<BK>(ch / CPR);
+                src = g + (int64_t)min(row0 + r, nrows - 1) * ld + k0 + lc * 8;
+            } else {
+                constexpr int CPR = ROWS / 8;
+                const int k = ch / CPR, lc = (ch % CPR) ^ rc_swz<ROWS>(ch / CPR);
+                src = g + (int64_t)(k0 + k) * ld + min(row0 + lc * 8, nrows - 8);
+            }
+            __builtin_amdgcn_global_load_lds(
+                (const void*)src, (__attribute__((address_space(3))) void*)(s + blk * 512), 16, 0,
+                0);
+        }
+    }
+
+    // MFMA fragment of tile rows r0..r0+31, reduction block kk (16 wide).
+    __device__ __forceinline__ static bf16x8 frag(const bf16* s, int r0, int kk, int lane) {
+        if constexpr (!RC) {
+            const int r = r0 + (lane & 31);
+            const int c = 2 * kk + (lane >> 5);
+            return *reinterpret_cast<const bf16x8*>(s + r * BK + ((c ^ pc_swz<BK>(r)) << 3));
+        } else {
+            const int grp = lane >> 4, i = lane & 15;
+            const int col = r0 + 16 * (grp & 1) + 4 * (i & 3);
+            const int k = kk * 16 + 8 * (grp >> 1) + (i >> 2);
+            const bf16* p0 = s + k * ROWS + (((col >> 3) ^ rc_swz<ROWS>(k)) << 3) + (col & 7);
+            const bf16* p1 =
+                s + (k + 4) * ROWS + (((col >> 3) ^ rc_swz<ROWS>(k + 4)) << 3) + (col & 7);
+            const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4i16*)(p0));
+            const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4i16*)(p1));
+            const v4i16 v[2] = {lo, hi};
+            return *reinterpret_cast<const bf16x8*>(v);
+        }
+    }
+
+    // Element (row r, reduction index k) of the staged tile.
+    __device__ __forceinline__ static float at(const bf16* s, int r, int k) {
+        if constexpr (!RC)
+            return (float)s[r * BK + ((((k >> 3) ^ pc_swz<BK>(r))) << 3) + (k & 7)];
+        else
+            return (float)s[k * ROWS + (((r >> 3) ^ rc_swz<ROWS>(k)) << 3) + (r & 7)];
+    }
+};
+
+// With rowsum != nullptr, the blocks of the first column tile also sum each X
+// row over their reduction range (for dW = dy^T x: the bias gradient).
+template <int BM, int BN, int BK, int WM, int WN, int GM, int S, bool XRC, bool YRC, int EPI>
+__global__ __launch_bounds__(WM* WN * 64) void gemm_lds_kernel(
+    void* __restrict__ out_, const bf16* __restrict__ X, const bf16* __restrict__ Y,
+    const bf16* __restrict__ bias, const bf16* __restrict__ residual, int M, int N, int K,
+    int ldx, int ldy, int ldo, int kchunk, int64_t split_stride, float* __restrict__ rowsum,
+    int64_t rowsum_stride) {
+    constexpr int NW = WM * WN, NT = NW * 64;
+    constexpr int TM = BM / WM, TN = BN / WN;
+    constexpr int FM = TM / 32, FN = TN / 32;
+    static_assert(FM * 32 == TM && FN * 32 == TN, "wave tiles are whole 32x32 MFMA tiles");
+    using XO = LdsOperand<BM, BK, NW, XRC>;
+    using YO = LdsOperand<BN, BK, NW, YRC>;
+    constexpr int NPW = XO::NPW + YO::NPW;  // load instructions per wave per stage
+    extern __shared__ __attribute__((aligned(16))) bf16 lds_ring[];
+    bf16* Xs = lds_ring;                  // [S][BM * BK]
+    bf16* Ys = lds_ring + S * XO::ELEMS;  // [S][BN * BK]
+
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int wm = wid % WM, wn = wid / WM;
+    int tm, tn;
+    tile_of<GM>(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
+    const int i0 = tm * BM, j0 = tn * BN;
+    const int kbeg = blockIdx.z * kchunk;
+    const int nk = (min(K, kbeg + kchunk) - kbeg) / BK;
+
+    floatx16 acc[FN][FM];
+#pragma unroll
+    for (int a = 0; a < FN; a++)
+#pragma unroll
+        for (int b = 0; b < FM; b++) acc[a][b] = floatx16{};
+
+#pragma unroll
+    for (int s = 0; s < S - 1; s++)
+        if (s < nk) {
+            XO::load(Xs + s * XO::ELEMS, X, ldx, M, i0, kbeg + s * BK, wid, lane);
+            YO::load(Ys + s * YO::ELEMS, Y, ldy, N, j0, kbeg + s * BK, wid, lane);
+        }
+
+    const bool do_rowsum = rowsum != nullptr && tn == 0 && tid < BM;
+    float rsum = 0.f;
+    const int fr = lane & 31, g = lane >> 5;
+    for (int kt = 0; kt < nk; kt++) {
+        const int pending = min(S - 2, nk - 1 - kt);
+        if (pending >= 3) wait_vmcnt<3 * NPW>();
+        else if (pending == 2) wait_vmcnt<2 * NPW>();
+        else if (pending == 1) wait_vmcnt<NPW>();
+        else wait_vmcnt<0>();
+        // This wave's reads of the buffer refilled below finished before its
+        // last MFMA of the previous step consumed them.
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        if (kt + S - 1 < nk) {
+            const int sn = (kt + S - 1) % S;
+            XO::load(Xs + sn * XO::ELEMS, X, ldx, M, i0, kbeg + (kt + S - 1) * BK, wid, lane);
+            YO::load(Ys + sn * YO::ELEMS, Y, ldy, N, j0, kbeg + (kt + S - 1) * BK, wid, lane);
+        }
+        const bf16* xb = Xs + (kt % S) * XO::ELEMS;
+        const bf16* yb = Ys + (kt % S) * YO::ELEMS;
+        if (do_rowsum)
+#pragma unroll 8
+            for (int k = 0; k < BK; k++) rsum += XO::at(xb, tid, k);
+        bf16x8 a[2][FN], b[2][FM];
+        auto read_frags = [&](int kk, bf16x8* af, bf16x8* bfr) {
+#pragma unroll
+            for (int f = 0; f < FN; f++) af[f] = YO::frag(yb, wn * TN + f * 32, kk, lane);
+#pragma unroll
+            for (int f = 0; f < FM; f++) bfr[f] = XO::frag(xb, wm * TM + f * 32, kk, lane);
+        };
+        read_frags(0, a[0], b[0]);
+#pragma unroll
+        for (int kk = 0; kk < BK / 16; kk++) {
+            if (kk + 1 < BK / 16) read_frags(kk + 1, a[(kk + 1) & 1], b[(kk + 1) & 1]);
+#pragma unroll
+            for (int fn = 0; fn < FN; fn++)
+#pragma unroll
+                for (int fm = 0; fm < FM; fm++)
+                    acc[fn][fm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        a[kk & 1][fn], b[kk & 1][fm], acc[fn][fm], 0, 0, 0);
+        }
+    }
+    if (do_rowsum && i0 + tid < M) rowsum[blockIdx.z * rowsum_stride + i0 + tid] = rsum;
+    (void)NT;
+
+    // epilogue: lane holds column i = l%32 of each tile and rows j in runs of 4
+#pragma unroll
+    for (int fn = 0; fn < FN; fn++)
+#pragma unroll
+        for (int fm = 0; fm < FM; fm++) {
+            const int i = i0 + wm * TM + fm * 32 + fr;
+            if (i >= M) continue;
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const int j = j0 + wn * TN + fn * 32 + 8 * q + 4 * g;
+                if (j >= N) continue;
+                float v0 = acc[fn][fm][4 * q], v1 = acc[fn][fm][4 * q + 1];
+                float v2 = acc[fn][fm][4 * q + 2], v3 = acc[fn][fm][4 * q + 3];
+                if (EPI == EPI_F32) {
+                    float* o = reinterpret_cast<float*>(out_) + blockIdx.z * split_stride +
+                               (int64_t)i * ldo + j;
+                    *reinterpret_cast<floatx4*>(o) = floatx4{v0, v1, v2, v3};
+                } else {
+                    if (bias) {
+                        const bf16x4 bv = *reinterpret_cast<const bf16x4*>(bias + j);
+                        v0 += (float)bv[0];
+                        v1 += (float)bv[1];
+                        v2 += (float)bv[2];
+                        v3 += (float)bv[3];
+                    }
+                    if (residual) {
+                        const bf16x4 rv =
+                            *reinterpret_cast<const bf16x4*>(residual + (int64_t)i * ldo + j);
+                        v0 += (float)rv[0];
+                        v1 += (float)rv[1];
+                        v2 += (float)rv[2];
+                        v3 += (float)rv[3];
+                    }
+                    *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(out_) + (int64_t)i * ldo + j) =
+                        bf16x4{(bf16)v0, (bf16)v1, (bf16)v2, (bf16)v3};
+                }
+            }
+        }
+}
+
+template <int BM, int BN, int BK, int WM, int WN, int GM, int S>
+struct GemmLds {
+    static constexpr int bm = BM, bn = BN, bk = BK;
+    static constexpr size_t lds_bytes = (size_t)S * (BM + BN) * BK * sizeof(bf16);
+
+    template <bool XRC, bool YRC, int EPI>
+    static void run(void* out, const bf16* X, const bf16* Y, const bf16* bias,
+                    const bf16* residual, int M, int N, int K, int ldx, int ldy, int ldo,
+                    int splits, int kchunk, int64_t split_stride, float* rowsum,
+                    int64_t rowsum_stride, hipStream_t st) {
+        const int tiles = ceil_div(M, BM) * ceil_div(N, BN);
+        dim3 grid(tiles, 1, splits);
+        gemm_lds_kernel<BM, BN, BK, WM, WN, GM, S, XRC, YRC, EPI>
+            <<<grid, WM * WN * 64, lds_bytes, st>>>(out, X, Y, bias, residual, M, N, K, ldx, ldy,
+                                                    ldo, kchunk, split_stride, rowsum,
+                                                    rowsum_stride);
+    }
+
+    // Raises the kernel's dynamic-LDS limit (needed above 64 KB); call once.
+    template <bool XRC, bool YRC, int EPI>
+    static hipError_t prepare() {
+        return hipFuncSetAttribute(
+            (const void*)gemm_lds_kernel<BM, BN, BK, WM, WN, GM, S, XRC, YRC, EPI>,
+            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
+    }
+};

@@ -1,200 +1,17 @@
-// bf16 matrix products on the gfx950 matrix cores (v_mfma_f32_32x32x16_bf16),
-// fp32 accumulation: out[i, j] = sum_p X(i, p) Y(j, p) (+ bias[j]) (+ residual[i, j]).
-//
-// Operand storage: an operand is either reduction-contiguous (X[i*ld + p]) or
-// row-contiguous (X[p*ld + i]). Every tile is staged into LDS
-// reduction-contiguous, which is what an MFMA fragment wants: lane l reads
-// 8 consecutive reduction elements (16 bytes) of tile row l % 32. A
-// row-contiguous operand is transposed on the way into LDS: a thread loads
-// 8 rows x 2 reduction steps (two 16-byte loads) and packs each row's pair
-// into one dword with v_perm_b32 before writing it.
+// The bf16 matrix products of the linear layers:
 //   forward  y  = x W^T      X = x  (p-contig), Y = W  (p-contig)
 //   backward dx = dy W       X = dy (p-contig), Y = W  (row-contig)
 //   backward dW = dy^T x     X = dy (row-contig), Y = x (row-contig)
-// The weight gradient reduces over all B*T rows; its few output tiles are
-// split along that reduction (grid z), each split writing an fp32 partial that
-// a second kernel sums in split order (deterministic).
-//
-// The MFMA "row" dimension is the output column j, so each lane's
-// accumulators hold runs of 4 consecutive j and stores are 8-byte (bf16) or
-// 16-byte (fp32) vectors along the contiguous output dimension.
-// Accumulator layout of the 32x32 product: lane l, register v holds
-// (row 8*(v/4) + 4*(l/32) + v%4, column l%32).
-#include "kernels.h"
+// Shapes whose reduction length is a multiple of 64 run on the direct-to-LDS
+// pipelined kernel (gemm_lds.h); others on the register-staged kernel
+// (gemm_mfma.h). The weight gradient reduces over all B*T rows; its few output
+// tiles are split along that reduction (grid z), each split writing an fp32
+// partial that a second kernel sums in split order (deterministic). The bias
+// gradient (column sums of dy) rides along in the same kernel.
+#include <mutex>
 
-typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float floatx16 __attribute__((ext_vector_type(16)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+#include "gemm_lds.h"
 
-#define LDS_PAD 8  // bf16 elements of padding per LDS row (spreads rows over banks)
-
-template <int ROWS, int BK, int NT, bool RC>
-struct Stager {
-    // p-contig: one chunk = 8 consecutive p of one row (16 B)
-    // row-contig: one chunk = 8 consecutive rows x 2 consecutive p (2 x 16 B)
-    static constexpr int NCHUNK = RC ? (ROWS / 8) * (BK / 2) : ROWS * BK / 8;
-    static constexpr int CH = (NCHUNK + NT - 1) / NT;
-    static constexpr int NV = RC ? 2 : 1;
-    u32x4 r[CH][NV];
-
-    // Global -> registers for the tile at (row0, k0); rows >= nrows and
-    // reduction indices >= kend read as zero.
-    __device__ __forceinline__ void load(const bf16* __restrict__ g, int ld, int nrows, int kend,
-                                         int row0, int k0, int tid) {
-#pragma unroll
-        for (int q = 0; q < CH; q++) {
-            const int c = tid + q * NT;
-#pragma unroll
-            for (int u = 0; u < NV; u++) r[q][u] = u32x4{0u, 0u, 0u, 0u};
-            if (c >= NCHUNK) continue;
-            if (!RC) {
-                const int row = c / (BK / 8), kc = (c % (BK / 8)) * 8;
-                if (row0 + row < nrows && k0 + kc < kend)
-                    r[q][0] = *reinterpret_cast<const u32x4*>(g + (int64_t)(row0 + row) * ld + k0 + kc);
-            } else {
-                const int pp = (c % (BK / 2)) * 2, rc = (c / (BK / 2)) * 8;
-                if (row0 + rc < nrows)
-#pragma unroll
-                    for (int u = 0; u < 2; u++)
-                        if (k0 + pp + u < kend)
-                            r[q][u] = *reinterpret_cast<const u32x4*>(
-                                g + (int64_t)(k0 + pp + u) * ld + row0 + rc);
-            }
-        }
-    }
-
-    // Registers -> LDS tile [ROWS][BK + LDS_PAD], reduction-contiguous.
-    __device__ __forceinline__ void store(bf16* __restrict__ s, int tid) {
-#pragma unroll
-        for (int q = 0; q < CH; q++) {
-            const int c = tid + q * NT;
-            if (c >= NCHUNK) continue;
-            if (!RC) {
-                const int row = c / (BK / 8), kc = (c % (BK / 8)) * 8;
-                *reinterpret_cast<u32x4*>(s + row * (BK + LDS_PAD) + kc) = r[q][0];
-            } else {
-                const int pp = (c % (BK / 2)) * 2, rc = (c / (BK / 2)) * 8;
-                unsigned int* d = reinterpret_cast<unsigned int*>(s + rc * (BK + LDS_PAD) + pp);
-                constexpr int DW = (BK + LDS_PAD) / 2;  // dwords per LDS row
-#pragma unroll
-                for (int w = 0; w < 4; w++) {
-                    // rows rc+2w (low halves) and rc+2w+1 (high halves): pair (p, p+1)
-                    d[(2 * w) * DW] = __builtin_amdgcn_perm(r[q][1][w], r[q][0][w], 0x05040100u);
-                    d[(2 * w + 1) * DW] = __builtin_amdgcn_perm(r[q][1][w], r[q][0][w], 0x07060302u);
-                }
-            }
-        }
-    }
-};
-
-// EPI_BF16: out bf16 = acc (+ bias) (+ residual);  EPI_F32: out fp32 = acc.
-enum { EPI_BF16 = 0, EPI_F32 = 1 };
-
-template <int BM, int BN, int BK, int WM, int WN, bool XRC, bool YRC, int EPI>
-__global__ __launch_bounds__(WM* WN * 64) void gemm_mfma_kernel(
-    void* __restrict__ out_, const bf16* __restrict__ X, const bf16* __restrict__ Y,
-    const bf16* __restrict__ bias, const bf16* __restrict__ residual, int M, int N, int K,
-    int ldx, int ldy, int ldo, int kchunk, int64_t split_stride) {
-    constexpr int NT = WM * WN * 64;
-    constexpr int TM = BM / WM, TN = BN / WN;  // wave tile (i extent, j extent)
-    constexpr int FM = TM / 32, FN = TN / 32;  // 32x32 MFMA tiles per wave
-    constexpr int LDR = BK + LDS_PAD;
-    __shared__ bf16 Xs[2][BM * LDR];
-    __shared__ bf16 Ys[2][BN * LDR];
-
-    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    const int wm = wid % WM, wn = wid / WM;
-    const int i0 = blockIdx.y * BM, j0 = blockIdx.x * BN;
-    const int kbeg = blockIdx.z * kchunk, kend = min(K, kbeg + kchunk);
-
-    Stager<BM, BK, NT, XRC> xs;
-    Stager<BN, BK, NT, YRC> ys;
-    floatx16 acc[FN][FM];
-#pragma unroll
-    for (int a = 0; a < FN; a++)
-#pragma unroll
-        for (int b = 0; b < FM; b++) acc[a][b] = floatx16{};
-
-    const int nk = (kend - kbeg + BK - 1) / BK;
-    xs.load(X, ldx, M, kend, i0, kbeg, tid);
-    ys.load(Y, ldy, N, kend, j0, kbeg, tid);
-    xs.store(Xs[0], tid);
-    ys.store(Ys[0], tid);
-    __syncthreads();
-
-    const int fr = lane & 31, fk = (lane >> 5) * 8;
-    for (int kt = 0; kt < nk; kt++) {
-        const int buf = kt & 1;
-        if (kt + 1 < nk) {
-            xs.load(X, ldx, M, kend, i0, kbeg + (kt + 1) * BK, tid);
-            ys.load(Y, ldy, N, kend, j0, kbeg + (kt + 1) * BK, tid);
-        }
-        const bf16* xb = Xs[buf] + (wm * TM + fr) * LDR + fk;
-        const bf16* yb = Ys[buf] + (wn * TN + fr) * LDR + fk;
-#pragma unroll
-        for (int kk = 0; kk < BK; kk += 16) {
-            bf16x8 a[FN], b[FM];
-#pragma unroll
-            for (int f = 0; f < FN; f++) a[f] = *reinterpret_cast<const bf16x8*>(yb + f * 32 * LDR + kk);
-#pragma unroll
-            for (int f = 0; f < FM; f++) b[f] = *reinterpret_cast<const bf16x8*>(xb + f * 32 * LDR + kk);
-#pragma unroll
-            for (int fn = 0; fn < FN; fn++)
-#pragma unroll
-                for (int fm = 0; fm < FM; fm++)
-                    acc[fn][fm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[fn], b[fm], acc[fn][fm],
-                                                                          0, 0, 0);
-        }
-        if (kt + 1 < nk) {
-            xs.store(Xs[buf ^ 1], tid);
-            ys.store(Ys[buf ^ 1], tid);
-        }
-        __syncthreads();
-    }
-
-    // epilogue: lane holds column i = l%32 of each tile and rows j in runs of 4
-#pragma unroll
-    for (int fn = 0; fn < FN; fn++)
-#pragma unroll
-        for (int fm = 0; fm < FM; fm++) {
-            const int i = i0 + wm * TM + fm * 32 + fr;
-            if (i >= M) continue;
-#pragma unroll
-            for (int g = 0; g < 4; g++) {
-                const int j = j0 + wn * TN + fn * 32 + 8 * g + 4 * (lane >> 5);
-                if (j >= N) continue;
-                float v0 = acc[fn][fm][4 * g], v1 = acc[fn][fm][4 * g + 1];
-                float v2 = acc[fn][fm][4 * g + 2], v3 = acc[fn][fm][4 * g + 3];
-                if (EPI == EPI_F32) {
-                    float* o = reinterpret_cast<float*>(out_) + blockIdx.z * split_stride +
-                               (int64_t)i * ldo + j;
-                    *reinterpret_cast<floatx4*>(o) = floatx4{v0, v1, v2, v3};
-                } else {
-                    if (bias) {
-                        const bf16x4 bv = *reinterpret_cast<const bf16x4*>(bias + j);
-                        v0 += (float)bv[0];
-                        v1 += (float)bv[1];
-                        v2 += (float)bv[2];
-                        v3 += (float)bv[3];
-                    }
-                    if (residual) {
-                        const bf16x4 rv =
-                            *reinterpret_cast<const bf16x4*>(residual + (int64_t)i * ldo + j);
-                        v0 += (float)rv[0];
-                        v1 += (float)rv[1];
-                        v2 += (float)rv[2];
-                        v3 += (float)rv[3];
-                    }
-                    bf16* o = reinterpret_cast<bf16*>(out_) + (int64_t)i * ldo + j;
-                    *reinterpret_cast<bf16x4*>(o) = bf16x4{(bf16)v0, (bf16)v1, (bf16)v2, (bf16)v3};
-                }
-            }
-        }
-}
-
-// out[e] = sum_z part[z * n + e], z in order (n % 4 == 0)
 __global__ __launch_bounds__(256) void split_reduce_kernel(float* __restrict__ out,
                                                            const float* __restrict__ part,
                                                            int splits, int64_t n) {
@@ -205,33 +22,51 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(float* __restrict__ o
     *reinterpret_cast<floatx4*>(out + i) = s;
 }
 
-constexpr int GBM = 128, GBN = 128, GBK = 32, GWM = 2, GWN = 2;
+using Cfg = GemmCfg<128, 128, 32, 2, 2, 16>;      // register-staged fallback
+using FwdCfg = GemmLds<256, 192, 64, 4, 2, 8, 2>;  // y = x W^T and dx = dy W
+using DwCfg = GemmLds<128, 128, 64, 2, 2, 8, 2>;   // dW = dy^T x
+constexpr int LDS_BK = 64;
 
-template <bool XRC, bool YRC, int EPI>
-static void launch(void* out, const bf16* X, const bf16* Y, const bf16* bias,
-                   const bf16* residual, int M, int N, int K, int ldx, int ldy, int ldo,
-                   int splits, int kchunk, int64_t split_stride, hipStream_t st) {
-    dim3 grid(ceil_div(N, GBN), ceil_div(M, GBM), splits);
-    gemm_mfma_kernel<GBM, GBN, GBK, GWM, GWN, XRC, YRC, EPI><<<grid, GWM * GWN * 64, 0, st>>>(
-        out, X, Y, bias, residual, M, N, K, ldx, ldy, ldo, kchunk, split_stride);
+// The direct-to-LDS kernels use more than 64 KB of LDS; raise their limits once.
+static void prepare_lds_kernels() {
+    static std::once_flag once;
+    std::call_once(once, [] {
+        (void)FwdCfg::prepare<false, false, EPI_BF16>();
+        (void)FwdCfg::prepare<false, true, EPI_BF16>();
+        (void)DwCfg::prepare<true, true, EPI_F32>();
+    });
 }
 
 // out[M,N] = inp[M,K] . w[N,K]^T (+ bias) (+ residual)
 void gemm_bf16_fwd(bf16* out, const bf16* inp, const bf16* w, const bf16* bias,
                    const bf16* residual, int M, int K, int N, hipStream_t st) {
-    launch<false, false, EPI_BF16>(out, inp, w, bias, residual, M, N, K, K, K, N, 1, K, 0, st);
+    if (K % LDS_BK == 0) {
+        prepare_lds_kernels();
+        FwdCfg::run<false, false, EPI_BF16>(out, inp, w, bias, residual, M, N, K, K, K, N, 1, K,
+                                            0, nullptr, 0, st);
+        return;
+    }
+    Cfg::run<false, false, EPI_BF16>(out, inp, w, bias, residual, M, N, K, K, K, N, 1, K, 0,
+                                     nullptr, 0, st);
 }
 
 // dinp[M,K] = dout[M,N] . w[N,K]
 void gemm_bf16_bwd_dx(bf16* dinp, const bf16* dout, const bf16* w, int M, int N, int K,
                       hipStream_t st) {
-    launch<false, true, EPI_BF16>(dinp, dout, w, nullptr, nullptr, M, K, N, N, K, K, 1, N, 0, st);
+    if (N % LDS_BK == 0) {
+        prepare_lds_kernels();
+        FwdCfg::run<false, true, EPI_BF16>(dinp, dout, w, nullptr, nullptr, M, K, N, N, K, K, 1,
+                                           N, 0, nullptr, 0, st);
+        return;
+    }
+    Cfg::run<false, true, EPI_BF16>(dinp, dout, w, nullptr, nullptr, M, K, N, N, K, K, 1, N, 0,
+                                    nullptr, 0, st);
 }
 
 // Splits of the B*T reduction of a weight gradient [N, K]: enough blocks to
 // cover the chip about four times over, each split at least 512 rows long.
 static int dw_splits(int M, int N, int K) {
-    const int tiles = ceil_div(N, GBM) * ceil_div(K, GBN);
+    const int tiles = ceil_div(N, DwCfg::bm) * ceil_div(K, DwCfg::bn);
     int s = (4 * 256 + tiles - 1) / tiles;
     const int smax = M / 512;
     if (s > smax) s = smax;
@@ -241,21 +76,35 @@ static int dw_splits(int M, int N, int K) {
 
 int64_t gemm_dw_workspace_floats(int M, int N, int K) {
     const int s = dw_splits(M, N, K);
-    return s > 1 ? (int64_t)s * N * K : 0;
+    return s > 1 ? (int64_t)s * N * (K + 1) : 0;
 }
 
-// dw[N,K] (fp32) = dout[M,N]^T . inp[M,K]; ws: gemm_dw_workspace_floats(M,N,K) floats
-void gemm_bf16_bwd_dw(float* dw, const bf16* dout, const bf16* inp, int M, int N, int K,
-                      float* ws, hipStream_t st) {
+// dw[N,K] (fp32) = dout[M,N]^T . inp[M,K] and, if db != nullptr,
+// db[N] = sum_m dout[m, :]; ws: gemm_dw_workspace_floats(M,N,K) floats
+// (split partials of dw, then of db).
+void gemm_bf16_bwd_dw(float* dw, float* db, const bf16* dout, const bf16* inp, int M, int N,
+                      int K, float* ws, hipStream_t st) {
     const int s = dw_splits(M, N, K);
+    const bool lds = M % LDS_BK == 0;
+    if (lds) prepare_lds_kernels();
+    auto launch = [&](void* out, int splits, int kchunk, int64_t stride, float* rs,
+                      int64_t rs_stride) {
+        if (lds)
+            DwCfg::run<true, true, EPI_F32>(out, dout, inp, nullptr, nullptr, N, K, M, N, K, K,
+                                            splits, kchunk, stride, rs, rs_stride, st);
+        else
+            Cfg::run<true, true, EPI_F32>(out, dout, inp, nullptr, nullptr, N, K, M, N, K, K,
+                                          splits, kchunk, stride, rs, rs_stride, st);
+    };
     if (s == 1) {
-        launch<true, true, EPI_F32>(dw, dout, inp, nullptr, nullptr, N, K, M, N, K, K, 1, M, 0, st);
+        launch(dw, 1, M, 0, db, 0);
         return;
     }
-    const int kchunk = ceil_div(ceil_div(M, s), GBK) * GBK;
+    const int kchunk = ceil_div(ceil_div(M, s), LDS_BK) * LDS_BK;
     const int splits = ceil_div(M, kchunk);
-    launch<true, true, EPI_F32>(ws, dout, inp, nullptr, nullptr, N, K, M, N, K, K, splits, kchunk,
-                                (int64_t)N * K, st);
     const int64_t n = (int64_t)N * K;
+    float* wsdb = ws + (int64_t)splits * n;
+    launch(ws, splits, kchunk, n, db ? wsdb : nullptr, N);
     split_reduce_kernel<<<ceil_div(n / 4, 256), 256, 0, st>>>(dw, ws, splits, n);
+    if (db) split_reduce_kernel<<<ceil_div(N / 4, 256), 256, 0, st>>>(db, wsdb, splits, N);
 }

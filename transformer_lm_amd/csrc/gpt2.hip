@@ -163,15 +163,15 @@ void plan(const gpt2_config* c, Layout* lay) {
 // Kernel classes for timing (gpt2_timing_arm / gpt2_timing_read).
 enum {
     K_ENCODER_FWD, K_LAYERNORM_FWD, K_MATMUL_FWD, K_ATTENTION_FWD, K_GELU_FWD, K_CLASSIFIER,
-    K_MATMUL_BWD_DX, K_MATMUL_BWD_DW, K_BIAS_BWD, K_GELU_BWD, K_LAYERNORM_BWD, K_ATTENTION_BWD,
+    K_MATMUL_BWD_DX, K_MATMUL_BWD_DW, K_GELU_BWD, K_LAYERNORM_BWD, K_ATTENTION_BWD,
     K_ENCODER_BWD, K_ADAMW, NUM_K
 };
 const char* const K_NAMES[NUM_K] = {
     "encoder_fwd", "layernorm_fwd", "matmul_fwd", "attention_fwd", "gelu_fwd", "classifier",
-    "matmul_bwd_dx", "matmul_bwd_dw", "bias_bwd", "gelu_bwd", "layernorm_bwd", "attention_bwd",
+    "matmul_bwd_dx", "matmul_bwd_dw", "gelu_bwd", "layernorm_bwd", "attention_bwd",
     "encoder_bwd", "adamw"};
 // 1: work is compulsory HBM bytes; 0: floating-point operations
-const int K_IS_BYTES[NUM_K] = {1, 1, 0, 0, 1, 1, 0, 0, 1, 1, 1, 0, 1, 1};
+const int K_IS_BYTES[NUM_K] = {1, 1, 0, 0, 1, 1, 0, 0, 1, 1, 0, 1, 1};
 
 }  // namespace
 
@@ -373,7 +373,6 @@ void backward_impl(gpt2* h) {
     float* dws = (float*)h->a[W_DW_SPLIT];
     // LayerNorm backward reads x and dy, reads+writes (or writes) dx
     auto ln_bytes = [&](bool acc) { return (acc ? 4.0 : 3.0) * nC * es + 8.0 * BT + C * (es + 8); };
-    auto bb_bytes = [&](double N) { return BT * N * es + 4.0 * N; };
     const double attn_flops = 8.0 * B * NH * (C / NH) * causal_pairs(Tn);
 
     // output head (tied to wte): dlnf = dz . wte; dwte = dz^T . lnf
@@ -383,7 +382,7 @@ void backward_impl(gpt2* h) {
     }
     {
         KScope k(h, K_MATMUL_BWD_DW, mm_flops(Vp, C, BT));
-        matmul_bwd_dw<T>(G[P_WTE], dlogits, lnf, BT, Vp, C, dws, st);
+        matmul_bwd_dw<T>(G[P_WTE], nullptr, dlogits, lnf, BT, Vp, C, dws, bp, st);
     }
     {
         KScope k(h, K_LAYERNORM_BWD, ln_bytes(false));
@@ -400,11 +399,8 @@ void backward_impl(gpt2* h) {
         }
         {
             KScope k(h, K_MATMUL_BWD_DW, mm_flops(C, 4 * C, BT));
-            matmul_bwd_dw<T>(G[P_FCPROJW] + w4, dres, fchg + l * 4 * nC, BT, C, 4 * C, dws, st);
-        }
-        {
-            KScope k(h, K_BIAS_BWD, bb_bytes(C));
-            bias_bwd<T>(G[P_FCPROJB] + l * C, dres, BT, C, bp, st);
+            matmul_bwd_dw<T>(G[P_FCPROJW] + w4, G[P_FCPROJB] + l * C, dres, fchg + l * 4 * nC, BT,
+                             C, 4 * C, dws, bp, st);
         }
         {
             KScope k(h, K_GELU_BWD, 3.0 * 4 * nC * es);
@@ -416,11 +412,8 @@ void backward_impl(gpt2* h) {
         }
         {
             KScope k(h, K_MATMUL_BWD_DW, mm_flops(4 * C, C, BT));
-            matmul_bwd_dw<T>(G[P_FCW] + w4, d4C, ln2 + l * nC, BT, 4 * C, C, dws, st);
-        }
-        {
-            KScope k(h, K_BIAS_BWD, bb_bytes(4 * C));
-            bias_bwd<T>(G[P_FCB] + l * 4 * C, d4C, BT, 4 * C, bp, st);
+            matmul_bwd_dw<T>(G[P_FCW] + w4, G[P_FCB] + l * 4 * C, d4C, ln2 + l * nC, BT, 4 * C, C,
+                             dws, bp, st);
         }
         {
             KScope k(h, K_LAYERNORM_BWD, ln_bytes(true));
@@ -436,11 +429,8 @@ void backward_impl(gpt2* h) {
         }
         {
             KScope k(h, K_MATMUL_BWD_DW, mm_flops(C, C, BT));
-            matmul_bwd_dw<T>(G[P_ATTPROJW] + w1, dres, atty + l * nC, BT, C, C, dws, st);
-        }
-        {
-            KScope k(h, K_BIAS_BWD, bb_bytes(C));
-            bias_bwd<T>(G[P_ATTPROJB] + l * C, dres, BT, C, bp, st);
+            matmul_bwd_dw<T>(G[P_ATTPROJW] + w1, G[P_ATTPROJB] + l * C, dres, atty + l * nC, BT, C,
+                             C, dws, bp, st);
         }
         {
             KScope k(h, K_ATTENTION_BWD, attn_flops);
@@ -453,11 +443,8 @@ void backward_impl(gpt2* h) {
         }
         {
             KScope k(h, K_MATMUL_BWD_DW, mm_flops(3 * C, C, BT));
-            matmul_bwd_dw<T>(G[P_QKVW] + w3, d3C, ln1 + l * nC, BT, 3 * C, C, dws, st);
-        }
-        {
-            KScope k(h, K_BIAS_BWD, bb_bytes(3 * C));
-            bias_bwd<T>(G[P_QKVB] + l * 3 * C, d3C, BT, 3 * C, bp, st);
+            matmul_bwd_dw<T>(G[P_QKVW] + w3, G[P_QKVB] + l * 3 * C, d3C, ln1 + l * nC, BT, 3 * C,
+                             C, dws, bp, st);
         }
         {
             KScope k(h, K_LAYERNORM_BWD, ln_bytes(true));

@@ -41,16 +41,18 @@ template <typename T>
 void matmul_bwd_dx(T* dinp, const T* dout, const T* w, int M, int N, int K, hipStream_t st);
 // dw[N,K] = dout[M,N]^T . inp[M,K] (fp32, written)
 template <typename T>
-// ws: gemm_dw_workspace_floats(M, N, K) floats (bf16 storage splits the M reduction)
-void matmul_bwd_dw(float* dw, const T* dout, const T* inp, int M, int N, int K, float* ws,
-                   hipStream_t st);
+// and, if db != nullptr, db[N] = sum_m dout[m,:] (fp32, written).
+// ws: gemm_dw_workspace_floats(M, N, K) floats (bf16 storage splits the M
+// reduction); bias_partials: bias_bwd_partials(M, N) floats (fp32 storage).
+void matmul_bwd_dw(float* dw, float* db, const T* dout, const T* inp, int M, int N, int K,
+                   float* ws, float* bias_partials, hipStream_t st);
 // the bf16 matrix-core kernels behind the three matmul entry points above
 void gemm_bf16_fwd(bf16* out, const bf16* inp, const bf16* w, const bf16* bias,
                    const bf16* residual, int M, int K, int N, hipStream_t st);
 void gemm_bf16_bwd_dx(bf16* dinp, const bf16* dout, const bf16* w, int M, int N, int K,
                       hipStream_t st);
-void gemm_bf16_bwd_dw(float* dw, const bf16* dout, const bf16* inp, int M, int N, int K,
-                      float* ws, hipStream_t st);
+void gemm_bf16_bwd_dw(float* dw, float* db, const bf16* dout, const bf16* inp, int M, int N,
+                      int K, float* ws, hipStream_t st);
 int64_t gemm_dw_workspace_floats(int M, int N, int K);
 // db[N] = sum_m dout[m,:] (fp32, written); partials: bias_bwd_partials(M, N) floats
 template <typename T>

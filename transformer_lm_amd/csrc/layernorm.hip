@@ -1,16 +1,18 @@
 // LayerNorm forward and backward over rows of C channels (C % 8 == 0,
-// C <= 2048). One wave64 per row; a lane holds up to 4 chunks of 8 channels
-// (chunk k of lane l covers channels (l + 64k) * 8 .. +7) in registers, so a
-// row is read from HBM once. Statistics and all sums are fp32.
+// C <= 2048), the operation llm.c writes out over bare float arrays (talk
+// "llm.c's Origin and the Future of LLM Compilers", chapter "Deconstructing
+// PyTorch Abstractions"). One wave64 per row; a lane holds up to NCH chunks of
+// 8 channels (chunk k of lane l covers channels (l + 64k) * 8 .. +7) in
+// registers, so a row is read from HBM once. NCH is 2 for C <= 1024 and 4
+// above. Statistics and all sums are fp32.
 #include "kernels.h"
 
 #define LN_EPS 1e-5f
-#define LN_CHUNKS 4
 #define LN_ROWS_PER_BLOCK 4
 
 // mu = mean(x); var = mean((x - mu)^2) (biased); r = 1/sqrt(var + eps);
 // y = (x - mu) r w + b. Saves mu and r.
-template <typename T>
+template <typename T, int NCH>
 __global__ __launch_bounds__(256) void layernorm_fwd_kernel(T* __restrict__ out,
                                                             float* __restrict__ mean,
                                                             float* __restrict__ rstd,
@@ -22,11 +24,11 @@ __global__ __launch_bounds__(256) void layernorm_fwd_kernel(T* __restrict__ out,
     const int row = blockIdx.x * LN_ROWS_PER_BLOCK + (threadIdx.x >> 6);
     if (row >= N) return;
     const T* x = inp + (int64_t)row * C;
-    float v[LN_CHUNKS][8];
+    float v[NCH][8];
     float s = 0.f;
 #pragma unroll
-    for (int k = 0; k < LN_CHUNKS; k++) {
-        int c = (lane + 64 * k) * 8;
+    for (int k = 0; k < NCH; k++) {
+        const int c = (lane + 64 * k) * 8;
         if (c < C) {
             load8(x + c, v[k]);
 #pragma unroll
@@ -36,19 +38,19 @@ __global__ __launch_bounds__(256) void layernorm_fwd_kernel(T* __restrict__ out,
     const float mu = wave_sum(s) / C;
     float ss = 0.f;
 #pragma unroll
-    for (int k = 0; k < LN_CHUNKS; k++) {
-        int c = (lane + 64 * k) * 8;
+    for (int k = 0; k < NCH; k++) {
+        const int c = (lane + 64 * k) * 8;
         if (c < C)
 #pragma unroll
             for (int i = 0; i < 8; i++) {
-                float d = v[k][i] - mu;
+                const float d = v[k][i] - mu;
                 ss += d * d;
             }
     }
     const float r = 1.f / sqrtf(wave_sum(ss) / C + LN_EPS);
 #pragma unroll
-    for (int k = 0; k < LN_CHUNKS; k++) {
-        int c = (lane + 64 * k) * 8;
+    for (int k = 0; k < NCH; k++) {
+        const int c = (lane + 64 * k) * 8;
         if (c < C) {
             float wv[8], bv[8], o[8];
             load8(w + c, wv);
@@ -67,8 +69,11 @@ __global__ __launch_bounds__(256) void layernorm_fwd_kernel(T* __restrict__ out,
 template <typename T>
 void layernorm_fwd(T* out, float* mean, float* rstd, const T* inp, const T* w, const T* b,
                    int N, int C, hipStream_t st) {
-    layernorm_fwd_kernel<T><<<ceil_div(N, LN_ROWS_PER_BLOCK), 256, 0, st>>>(out, mean, rstd, inp,
-                                                                           w, b, N, C);
+    const int grid = ceil_div(N, LN_ROWS_PER_BLOCK);
+    if (C <= 1024)
+        layernorm_fwd_kernel<T, 2><<<grid, 256, 0, st>>>(out, mean, rstd, inp, w, b, N, C);
+    else
+        layernorm_fwd_kernel<T, 4><<<grid, 256, 0, st>>>(out, mean, rstd, inp, w, b, N, C);
 }
 
 // Backward. With xhat = (x - mu) r and g = w dy:
@@ -76,20 +81,20 @@ void layernorm_fwd(T* out, float* mean, float* rstd, const T* inp, const T* w, c
 // dw = sum_rows dy xhat and db = sum_rows dy are reduced deterministically:
 // each block walks a fixed set of rows, its four waves' register sums are
 // combined in wave order through LDS into one partial row per block, and a
-// second kernel sums the partial rows in block order.
+// second kernel sums the partial rows in a fixed order.
 #define LN_BWD_BLOCKS 1024
 
-template <typename T>
+template <typename T, int NCH>
 __global__ __launch_bounds__(256) void layernorm_bwd_kernel(
     T* dinp, int accumulate, const T* __restrict__ dout, const T* __restrict__ inp,
     const T* __restrict__ w, const float* __restrict__ mean, const float* __restrict__ rstd,
     int N, int C, float* __restrict__ partials) {
     __shared__ float red[2 * 2048];
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    float dw[LN_CHUNKS][8], db[LN_CHUNKS][8], wv[LN_CHUNKS][8];
+    float dw[NCH][8], db[NCH][8], wv[NCH][8];
 #pragma unroll
-    for (int k = 0; k < LN_CHUNKS; k++) {
-        int c = (lane + 64 * k) * 8;
+    for (int k = 0; k < NCH; k++) {
+        const int c = (lane + 64 * k) * 8;
 #pragma unroll
         for (int i = 0; i < 8; i++) dw[k][i] = db[k][i] = 0.f;
         if (c < C) load8(w + c, wv[k]);
@@ -97,18 +102,18 @@ __global__ __launch_bounds__(256) void layernorm_bwd_kernel(
     for (int row = blockIdx.x * LN_ROWS_PER_BLOCK + wid; row < N;
          row += gridDim.x * LN_ROWS_PER_BLOCK) {
         const float mu = mean[row], r = rstd[row];
-        float xh[LN_CHUNKS][8], dy[LN_CHUNKS][8];
+        float xh[NCH][8], dy[NCH][8];
         float gs = 0.f, gxs = 0.f;
 #pragma unroll
-        for (int k = 0; k < LN_CHUNKS; k++) {
-            int c = (lane + 64 * k) * 8;
+        for (int k = 0; k < NCH; k++) {
+            const int c = (lane + 64 * k) * 8;
             if (c < C) {
                 load8(inp + (int64_t)row * C + c, xh[k]);
                 load8(dout + (int64_t)row * C + c, dy[k]);
 #pragma unroll
                 for (int i = 0; i < 8; i++) {
                     xh[k][i] = (xh[k][i] - mu) * r;
-                    float g = wv[k][i] * dy[k][i];
+                    const float g = wv[k][i] * dy[k][i];
                     gs += g;
                     gxs += g * xh[k][i];
                     dw[k][i] += dy[k][i] * xh[k][i];
@@ -118,14 +123,14 @@ __global__ __launch_bounds__(256) void layernorm_bwd_kernel(
         }
         const float gm = wave_sum(gs) / C, gxm = wave_sum(gxs) / C;
 #pragma unroll
-        for (int k = 0; k < LN_CHUNKS; k++) {
-            int c = (lane + 64 * k) * 8;
+        for (int k = 0; k < NCH; k++) {
+            const int c = (lane + 64 * k) * 8;
             if (c < C) {
                 float o[8];
                 if (accumulate) load8(dinp + (int64_t)row * C + c, o);
 #pragma unroll
                 for (int i = 0; i < 8; i++) {
-                    float dx = (wv[k][i] * dy[k][i] - gm - xh[k][i] * gxm) * r;
+                    const float dx = (wv[k][i] * dy[k][i] - gm - xh[k][i] * gxm) * r;
                     o[i] = accumulate ? o[i] + dx : dx;
                 }
                 store8(dinp + (int64_t)row * C + c, o);
@@ -136,8 +141,8 @@ __global__ __launch_bounds__(256) void layernorm_bwd_kernel(
     for (int q = 0; q < LN_ROWS_PER_BLOCK; q++) {
         if (wid == q) {
 #pragma unroll
-            for (int k = 0; k < LN_CHUNKS; k++) {
-                int c = (lane + 64 * k) * 8;
+            for (int k = 0; k < NCH; k++) {
+                const int c = (lane + 64 * k) * 8;
                 if (c < C)
 #pragma unroll
                     for (int i = 0; i < 8; i++) {
@@ -155,20 +160,23 @@ __global__ __launch_bounds__(256) void layernorm_bwd_kernel(
     }
 }
 
-// 64 partial columns per block, 4 row phases per column combined in order.
-__global__ __launch_bounds__(256) void layernorm_bwd_reduce_kernel(
+// Sums the partial rows: a block owns 64 columns, its 16 row phases walk the
+// rows with stride 16 and are combined in phase order.
+__global__ __launch_bounds__(1024) void layernorm_bwd_reduce_kernel(
     float* __restrict__ dw, float* __restrict__ db, const float* __restrict__ partials,
     int nblocks, int C) {
-    __shared__ float red[4][64];
+    __shared__ float red[16][64];
     const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
     const int j = blockIdx.x * 64 + tx;
     float s = 0.f;
     if (j < 2 * C)
-        for (int b = ty; b < nblocks; b += 4) s += partials[(int64_t)b * 2 * C + j];
+        for (int b = ty; b < nblocks; b += 16) s += partials[(int64_t)b * 2 * C + j];
     red[ty][tx] = s;
     __syncthreads();
     if (ty == 0 && j < 2 * C) {
-        const float t = ((red[0][tx] + red[1][tx]) + red[2][tx]) + red[3][tx];
+        float t = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; r++) t += red[r][tx];
         if (j < C)
             dw[j] = t;
         else
@@ -184,9 +192,13 @@ void layernorm_bwd(T* dinp, int accumulate, float* dw, float* db, const T* dout,
                    float* partials, hipStream_t st) {
     int nb = ceil_div(N, LN_ROWS_PER_BLOCK);
     if (nb > LN_BWD_BLOCKS) nb = LN_BWD_BLOCKS;
-    layernorm_bwd_kernel<T><<<nb, 256, 0, st>>>(dinp, accumulate, dout, inp, w, mean, rstd, N, C,
-                                                partials);
-    layernorm_bwd_reduce_kernel<<<ceil_div(2 * C, 64), 256, 0, st>>>(dw, db, partials, nb, C);
+    if (C <= 1024)
+        layernorm_bwd_kernel<T, 2><<<nb, 256, 0, st>>>(dinp, accumulate, dout, inp, w, mean, rstd,
+                                                       N, C, partials);
+    else
+        layernorm_bwd_kernel<T, 4><<<nb, 256, 0, st>>>(dinp, accumulate, dout, inp, w, mean, rstd,
+                                                       N, C, partials);
+    layernorm_bwd_reduce_kernel<<<ceil_div(2 * C, 64), 1024, 0, st>>>(dw, db, partials, nb, C);
 }
 
 template void layernorm_fwd<float>(float*, float*, float*, const float*, const float*,

@@ -118,14 +118,16 @@ void matmul_bwd_dx(T* dinp, const T* dout, const T* w, int M, int N, int K, hipS
 }
 
 template <typename T>
-void matmul_bwd_dw(float* dw, const T* dout, const T* inp, int M, int N, int K, float* ws,
-                   hipStream_t st) {
-    // dw[n, k] = sum_m dout[m, n] inp[m, k]
-    if constexpr (std::is_same<T, bf16>::value)
-        gemm_bf16_bwd_dw(dw, dout, inp, M, N, K, ws, st);
-    else
+void matmul_bwd_dw(float* dw, float* db, const T* dout, const T* inp, int M, int N, int K,
+                   float* ws, float* bias_partials, hipStream_t st) {
+    // dw[n, k] = sum_m dout[m, n] inp[m, k]; db[n] = sum_m dout[m, n]
+    if constexpr (std::is_same<T, bf16>::value) {
+        gemm_bf16_bwd_dw(dw, db, dout, inp, M, N, K, ws, st);
+    } else {
         gemm_generic<T, T, float, float>(dw, dout, inp, nullptr, nullptr, N, K, M, 1, N, 1, K, K,
                                          st);
+        if (db) bias_bwd<T>(db, dout, M, N, bias_partials, st);
+    }
 }
 
 // Bias gradient db[n] = sum_m dout[m, n], deterministic two-stage column sum.
@@ -186,8 +188,8 @@ void bias_bwd(float* db, const T* dout, int M, int N, float* partials, hipStream
     template void matmul_fwd<T>(T*, const T*, const T*, const T*, const T*, int, int, int,      \
                                 hipStream_t);                                                  \
     template void matmul_bwd_dx<T>(T*, const T*, const T*, int, int, int, hipStream_t);         \
-    template void matmul_bwd_dw<T>(float*, const T*, const T*, int, int, int, float*,          \
-                                   hipStream_t);                                               \
+    template void matmul_bwd_dw<T>(float*, float*, const T*, const T*, int, int, int, float*,  \
+                                   float*, hipStream_t);                                       \
     template void bias_bwd<T>(float*, const T*, int, int, float*, hipStream_t);
 INST(float)
 INST(bf16)
