@@ -1,33 +1,36 @@
 // Causal attention for head size 64 in bf16 on the gfx950 matrix cores
 // (v_mfma_f32_32x32x16_bf16), the fused online-softmax attention of page
 // "llm.c: Large Language Model Training in Pure C/CUDA Without Dependencies"
-// (section "Fused Attention Kernel"): scores never go to HBM; K and V tiles of
-// 64 keys are staged in LDS; the backward pass rebuilds P from the saved
-// log-sum-exp.
+// (section "Fused Attention Kernel"): scores never go to HBM; 64-row tiles of
+// K, V (forward, dQ) or Q, dO (dK/dV) stream through a double-buffered LDS
+// ring filled by direct global -> LDS loads; the backward pass rebuilds P from
+// the saved log-sum-exp.
 //
-// Layout choices. A 32x32 MFMA accumulator gives lane l the column l%32 and
-// rows 8*(v/4) + 4*(l/32) + v%4 (register v). Score tiles are computed with
-// queries as columns where a kernel needs per-query statistics in one lane
-// (S^T = K Q^T), and with keys as columns where it needs per-key sums (S = Q K^T).
-// The MFMA reduction order inside a 16-wide k block is free as long as both
-// operands use the same one, so probabilities / score gradients feed the next
-// product straight from the accumulator registers: register v (0..7 of a
-// half-tile) of lane group g stands for reduction index 4g + v%4 + 8*(v/4), and
-// the other operand is read from a transposed LDS tile in the same order
-// (two 8-byte reads).
+// Tiles keep their global layout in LDS: [64 rows][64 dims], 128-byte rows
+// whose 16-byte chunks are XOR-permuted (chunk c of row r at c ^ swz(r)).
+// Fragments with dims as the reduction come from one ds_read_b128; fragments
+// with tile rows as the reduction (V^T, K^T, Q^T, dO^T) come from two
+// ds_read_b64_tr_b16 transpose reads, which give lane o of a 16-lane group
+// column c0+o of rows k0..k0+3 when lane i points at row k0 + i/4,
+// columns c0 + 4*(i%4).
+//
+// A 32x32 accumulator gives lane l the column l%32 and rows
+// 8*(v/4) + 4*(l/32) + v%4 (register v). Score tiles are computed with queries
+// as columns where a kernel needs per-query statistics in one lane
+// (S^T = K Q^T), and with keys as columns where it needs per-key sums
+// (S = Q K^T). The reduction order inside an MFMA is free as long as both
+// operands use the same one, so probabilities and score gradients feed the
+// next product straight from the accumulator registers: register v (0..7 of a
+// half tile) of lane group g stands for tile row 4g + v%4 + 8*(v/4), and the
+// transpose reads fetch the other operand's rows in that order.
 //
 // Softmax runs in base 2: x = s * log2(e) / sqrt(hs), p = exp2(x - m).
-#include "kernels.h"
-
-typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float floatx16 __attribute__((ext_vector_type(16)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
+#include "gemm_lds.h"
 
 #define HS 64
-#define LDR 72          // LDS row pitch in bf16 (64 + 8 padding)
-#define Q_PER_BLOCK 128 // 4 waves x 32 rows
-#define KV_TILE 64
+#define Q_PER_BLOCK 128  // 4 waves x 32 rows
+#define TILE 64          // rows of a streamed K/V or Q/dO tile
+#define TILE_ELEMS (TILE * HS)
 #define LOG2E 1.4426950408889634f
 #define LN2 0.6931471805599453f
 
@@ -37,12 +40,41 @@ __device__ __forceinline__ floatx16 mfma(bf16x8 a, bf16x8 b, floatx16 c) {
 
 __device__ __forceinline__ bf16x8 ld16(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
-// Two 4-element runs (reduction indices base..base+3 and base+8..base+11) of an
-// LDS row, as one MFMA fragment in the accumulator-register order.
-__device__ __forceinline__ bf16x8 ld_runs(const bf16* row, int base) {
-    const bf16x4 lo = *reinterpret_cast<const bf16x4*>(row + base);
-    const bf16x4 hi = *reinterpret_cast<const bf16x4*>(row + base + 8);
-    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+__device__ __forceinline__ int tswz(int r) { return pc_swz<64>(r); }
+
+// Direct loads of rows r0..r0+63 of a 64-wide head slice (row stride ld) into
+// the LDS tile s; rows >= nrows repeat row nrows-1. 4 waves, 2 loads each.
+__device__ __forceinline__ void dma_tile(bf16* s, const bf16* __restrict__ g, int64_t ld, int r0,
+                                         int nrows, int wid, int lane) {
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+        const int blk = wid * 2 + j, ch = blk * 64 + lane;
+        const int r = ch >> 3, lc = (ch & 7) ^ tswz(ch >> 3);
+        const bf16* src = g + (int64_t)min(r0 + r, nrows - 1) * ld + lc * 8;
+        __builtin_amdgcn_global_load_lds((const void*)src,
+                                         (__attribute__((address_space(3))) void*)(s + blk * 512),
+                                         16, 0, 0);
+    }
+}
+
+// Fragment with tile rows r0..r0+31 as MFMA rows and dims 16kk.. as reduction.
+__device__ __forceinline__ bf16x8 frag_rows(const bf16* s, int r0, int kk, int lane) {
+    const int r = r0 + (lane & 31), c = 2 * kk + (lane >> 5);
+    return ld16(s + r * HS + ((c ^ tswz(r)) << 3));
+}
+
+// Fragment with dims d0..d0+31 as MFMA rows and tile rows as reduction, in the
+// accumulator order: lane group g takes rows base+4g..+3 and base+8+4g..+3.
+__device__ __forceinline__ bf16x8 frag_dims(const bf16* s, int d0, int base, int lane) {
+    const int i = lane & 15, g = lane >> 5;
+    const int col = d0 + 16 * ((lane >> 4) & 1) + 4 * (i & 3);
+    const int ra = base + 4 * g + (i >> 2), rb = ra + 8;
+    const bf16* pa = s + ra * HS + (((col >> 3) ^ tswz(ra)) << 3) + (col & 7);
+    const bf16* pb = s + rb * HS + (((col >> 3) ^ tswz(rb)) << 3) + (col & 7);
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)pa);
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)pb);
+    const v4i16 v[2] = {lo, hi};
+    return *reinterpret_cast<const bf16x8*>(v);
 }
 
 // Registers 8*hh .. 8*hh+7 of an accumulator, rounded to bf16.
@@ -53,24 +85,12 @@ __device__ __forceinline__ bf16x8 half_tile(const floatx16& a, int hh) {
     return r;
 }
 
-// Stages rows [r0, r0 + 64) of a 64-wide head slice (row stride ld) into LDS,
-// row-major (rows x 64, pitch LDR) and/or transposed (64 x rows, pitch LDR).
-// Rows >= nrows read as zero. 256 threads, two 8-element chunks each.
-template <bool ROWMAJOR, bool TRANSPOSED>
-__device__ __forceinline__ void stage64(bf16* __restrict__ rm, bf16* __restrict__ tr,
-                                        const bf16* __restrict__ g, int64_t ld, int r0,
-                                        int nrows, int tid) {
-#pragma unroll
-    for (int q = 0; q < 2; q++) {
-        const int c = tid + q * 256;
-        const int r = c >> 3, d = (c & 7) * 8;
-        bf16x8 v = {};
-        if (r0 + r < nrows) v = ld16(g + (int64_t)(r0 + r) * ld + d);
-        if (ROWMAJOR) *reinterpret_cast<bf16x8*>(rm + r * LDR + d) = v;
-        if (TRANSPOSED)
-#pragma unroll
-            for (int e = 0; e < 8; e++) tr[(d + e) * LDR + r] = v[e];
-    }
+// The next tile may be requested once every wave has finished reading the
+// buffer it refills; the current one is usable once this wave's loads landed
+// and all waves passed the barrier.
+__device__ __forceinline__ void tile_barrier() {
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
 }
 
 // ---------------------------------------------------------------- forward --
@@ -81,8 +101,11 @@ __global__ __launch_bounds__(256) void flash_fwd_kernel(bf16* __restrict__ out,
                                                         float* __restrict__ lse,
                                                         const bf16* __restrict__ qkv, int Tn,
                                                         int C, int NH) {
-    __shared__ bf16 Ks[KV_TILE * LDR];
-    __shared__ bf16 Vt[HS * LDR];
+    // the tile ring lives in dynamic LDS: the compiler does not then make
+    // reads of one buffer wait for the direct loads into the other
+    extern __shared__ __attribute__((aligned(16))) bf16 ring[];
+    auto Ks = [&](int i) { return ring + i * TILE_ELEMS; };
+    auto Vs = [&](int i) { return ring + (2 + i) * TILE_ELEMS; };
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, g = lane >> 5;
     const int qt = gridDim.x - 1 - blockIdx.x;  // longest rows first
     const int bh = blockIdx.y, b = bh / NH, h = bh % NH;
@@ -99,19 +122,24 @@ __global__ __launch_bounds__(256) void flash_fwd_kernel(bf16* __restrict__ out,
     floatx16 o[2] = {floatx16{}, floatx16{}};
     float m = -INFINITY, l = 0.f;
 
-    const int kv_end = min(Tn, (qt + 1) * Q_PER_BLOCK);
-    for (int k0 = 0; k0 < kv_end; k0 += KV_TILE) {
-        __syncthreads();
-        stage64<true, false>(Ks, nullptr, base + C, C3, k0, Tn, tid);
-        stage64<false, true>(nullptr, Vt, base + 2 * C, C3, k0, Tn, tid);
-        __syncthreads();
+    const int ntiles = (min(Tn, (qt + 1) * Q_PER_BLOCK) + TILE - 1) / TILE;
+    dma_tile(Ks(0), base + C, C3, 0, Tn, wid, lane);
+    dma_tile(Vs(0), base + 2 * C, C3, 0, Tn, wid, lane);
+    for (int t = 0; t < ntiles; t++) {
+        const int buf = t & 1, k0 = t * TILE;
+        tile_barrier();
+        if (t + 1 < ntiles) {
+            dma_tile(Ks(buf ^ 1), base + C, C3, k0 + TILE, Tn, wid, lane);
+            dma_tile(Vs(buf ^ 1), base + 2 * C, C3, k0 + TILE, Tn, wid, lane);
+        }
         if (k0 > q0 + 31 || q0 >= Tn) continue;  // every key of the tile is masked
+        const bf16* kt_s = Ks(buf);
+        const bf16* vt_s = Vs(buf);
         floatx16 s[2] = {floatx16{}, floatx16{}};
 #pragma unroll
         for (int kt = 0; kt < 2; kt++)
 #pragma unroll
-            for (int kb = 0; kb < 4; kb++)
-                s[kt] = mfma(ld16(Ks + (32 * kt + (lane & 31)) * LDR + kb * 16 + 8 * g), qf[kb], s[kt]);
+            for (int kb = 0; kb < 4; kb++) s[kt] = mfma(frag_rows(kt_s, 32 * kt, kb, lane), qf[kb], s[kt]);
         float mx = -INFINITY;
 #pragma unroll
         for (int kt = 0; kt < 2; kt++)
@@ -144,10 +172,9 @@ __global__ __launch_bounds__(256) void flash_fwd_kernel(bf16* __restrict__ out,
 #pragma unroll
             for (int hh = 0; hh < 2; hh++) {
                 const bf16x8 pb = half_tile(s[kt], hh);
-                const int kk = 32 * kt + 16 * hh + 4 * g;
 #pragma unroll
                 for (int dt = 0; dt < 2; dt++)
-                    o[dt] = mfma(ld_runs(Vt + (32 * dt + (lane & 31)) * LDR, kk), pb, o[dt]);
+                    o[dt] = mfma(frag_dims(vt_s, 32 * dt, 32 * kt + 16 * hh, lane), pb, o[dt]);
             }
     }
     if (ql < Tn) {
@@ -168,20 +195,24 @@ __global__ __launch_bounds__(256) void flash_fwd_kernel(bf16* __restrict__ out,
 
 // ------------------------------------------------------------ backward dK dV --
 // Block: 128 keys of one (b, h); wave w owns keys kw .. kw+31, lane l the key
-// kw + l%32. Per 64-query tile (queries >= the block's first key):
-// S = Q K^T and dP = dO V^T (queries x keys), P = exp2(S*c - lse2),
-// dS = P (dP - D); dV^T += dO^T P; dK^T += Q^T dS.
+// kw + l%32. Per 64-query tile (queries >= the block's first key), in two
+// 32-query halves: S = Q K^T and dP = dO V^T (queries x keys),
+// P = exp2(S*c - lse2), dS = P (dP - D); dV^T += dO^T P; dK^T += Q^T dS.
 __global__ __launch_bounds__(256) void flash_bwd_dkv_kernel(
     bf16* __restrict__ dqkv, const bf16* __restrict__ dout, const bf16* __restrict__ qkv,
     const float* __restrict__ lse, const float* __restrict__ Dbuf, int Tn, int C, int NH) {
-    __shared__ bf16 Qs[KV_TILE * LDR], Qt[HS * LDR], dOs[KV_TILE * LDR], dOt[HS * LDR];
-    __shared__ __attribute__((aligned(16))) float ls[KV_TILE];
-    __shared__ __attribute__((aligned(16))) float Ds[KV_TILE];
+    extern __shared__ __attribute__((aligned(16))) bf16 ring[];
+    auto Qs = [&](int i) { return ring + i * TILE_ELEMS; };
+    auto Os = [&](int i) { return ring + (2 + i) * TILE_ELEMS; };
+    auto ls = [&](int i) { return reinterpret_cast<float*>(ring + 4 * TILE_ELEMS) + i * TILE; };
+    auto Ds = [&](int i) { return reinterpret_cast<float*>(ring + 4 * TILE_ELEMS) + (2 + i) * TILE; };
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, g = lane >> 5;
     const int bh = blockIdx.y, b = bh / NH, h = bh % NH;
     const int C3 = 3 * C;
     const bf16* base = qkv + (int64_t)b * Tn * C3 + h * HS;
     const bf16* dbase = dout + (int64_t)b * Tn * C + h * HS;
+    const float* lrow = lse + (int64_t)bh * Tn;
+    const float* Drow = Dbuf + (int64_t)bh * Tn;
     const int kb0 = blockIdx.x * Q_PER_BLOCK;
     const int kw = kb0 + wid * 32;
     const int kl = kw + (lane & 31);
@@ -195,55 +226,62 @@ __global__ __launch_bounds__(256) void flash_bwd_dkv_kernel(
     }
     floatx16 dk[2] = {floatx16{}, floatx16{}}, dv[2] = {floatx16{}, floatx16{}};
 
-    for (int q0 = kb0 & ~(KV_TILE - 1); q0 < Tn; q0 += KV_TILE) {
-        __syncthreads();
-        stage64<true, true>(Qs, Qt, base, C3, q0, Tn, tid);
-        stage64<true, true>(dOs, dOt, dbase, C, q0, Tn, tid);
-        if (tid < KV_TILE) {
-            const int q = q0 + tid;
-            ls[tid] = q < Tn ? lse[(int64_t)bh * Tn + q] * LOG2E : 0.f;
-            Ds[tid] = q < Tn ? Dbuf[(int64_t)bh * Tn + q] : 0.f;
+    // tile t covers queries kb0 + 64 t ..; the per-query statistics come along
+    // by direct loads (wave 2: log-sum-exp, wave 3: D), one float per lane
+    auto issue = [&](int t, int buf) {
+        const int q0 = kb0 + t * TILE;
+        dma_tile(Qs(buf), base, C3, q0, Tn, wid, lane);
+        dma_tile(Os(buf), dbase, C, q0, Tn, wid, lane);
+        if (wid >= 2) {
+            const float* src = (wid == 2 ? lrow : Drow) + min(q0 + lane, Tn - 1);
+            float* dst = wid == 2 ? ls(buf) : Ds(buf);
+            __builtin_amdgcn_global_load_lds((const void*)src,
+                                             (__attribute__((address_space(3))) void*)dst, 4, 0, 0);
         }
-        __syncthreads();
-        if (kw > q0 + KV_TILE - 1 || kw >= Tn) continue;  // no query of the tile sees these keys
-        floatx16 s[2] = {floatx16{}, floatx16{}}, dp[2] = {floatx16{}, floatx16{}};
+    };
+    const int ntiles = (Tn - kb0 + TILE - 1) / TILE;
+    if (ntiles > 0) issue(0, 0);
+    for (int t = 0; t < ntiles; t++) {
+        const int buf = t & 1, q0 = kb0 + t * TILE;
+        tile_barrier();
+        if (t + 1 < ntiles) issue(t + 1, buf ^ 1);
+        if (kw > q0 + TILE - 1 || kw >= Tn) continue;  // no query of the tile sees these keys
+        const bf16* qs = Qs(buf);
+        const bf16* os = Os(buf);
 #pragma unroll
-        for (int qt = 0; qt < 2; qt++)
+        for (int qt = 0; qt < 2; qt++) {
+            floatx16 s = floatx16{}, dp = floatx16{};
 #pragma unroll
             for (int kb = 0; kb < 4; kb++) {
-                const int ro = (32 * qt + (lane & 31)) * LDR + kb * 16 + 8 * g;
-                s[qt] = mfma(ld16(Qs + ro), kf[kb], s[qt]);
-                dp[qt] = mfma(ld16(dOs + ro), vf[kb], dp[qt]);
+                s = mfma(frag_rows(qs, 32 * qt, kb, lane), kf[kb], s);
+                dp = mfma(frag_rows(os, 32 * qt, kb, lane), vf[kb], dp);
             }
-#pragma unroll
-        for (int qt = 0; qt < 2; qt++)
 #pragma unroll
             for (int r = 0; r < 4; r++) {
                 const int qo = 32 * qt + 8 * r + 4 * g;  // 4 consecutive queries
-                const floatx4 l4 = *reinterpret_cast<const floatx4*>(ls + qo);
-                const floatx4 d4 = *reinterpret_cast<const floatx4*>(Ds + qo);
+                const floatx4 l4 = *reinterpret_cast<const floatx4*>(&ls(buf)[qo]);
+                const floatx4 d4 = *reinterpret_cast<const floatx4*>(&Ds(buf)[qo]);
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
                     const int q = q0 + qo + e, v = 4 * r + e;
-                    const float p = (kl <= q && q < Tn) ? exp2f(s[qt][v] * sc - l4[e]) : 0.f;
-                    s[qt][v] = p;
-                    dp[qt][v] = p * (dp[qt][v] - d4[e]);
+                    const float p =
+                        (kl <= q && q < Tn) ? exp2f(s[v] * sc - l4[e] * LOG2E) : 0.f;
+                    s[v] = p;
+                    dp[v] = p * (dp[v] - d4[e]);
                 }
             }
-#pragma unroll
-        for (int qt = 0; qt < 2; qt++)
 #pragma unroll
             for (int hh = 0; hh < 2; hh++) {
-                const bf16x8 pb = half_tile(s[qt], hh);
-                const bf16x8 db = half_tile(dp[qt], hh);
-                const int qq = 32 * qt + 16 * hh + 4 * g;
+                const bf16x8 pb = half_tile(s, hh);
+                const bf16x8 db = half_tile(dp, hh);
+                const int rb = 32 * qt + 16 * hh;
 #pragma unroll
                 for (int dt = 0; dt < 2; dt++) {
-                    const int ro = (32 * dt + (lane & 31)) * LDR;
-                    dv[dt] = mfma(ld_runs(dOt + ro, qq), pb, dv[dt]);
-                    dk[dt] = mfma(ld_runs(Qt + ro, qq), db, dk[dt]);
+                    dv[dt] = mfma(frag_dims(os, 32 * dt, rb, lane), pb, dv[dt]);
+                    dk[dt] = mfma(frag_dims(qs, 32 * dt, rb, lane), db, dk[dt]);
                 }
             }
+        }
     }
     if (kl < Tn) {
         bf16* krow = dqkv + ((int64_t)b * Tn + kl) * C3 + C + h * HS;
@@ -270,7 +308,9 @@ __global__ __launch_bounds__(256) void flash_bwd_dkv_kernel(
 __global__ __launch_bounds__(256) void flash_bwd_dq_kernel(
     bf16* __restrict__ dqkv, const bf16* __restrict__ dout, const bf16* __restrict__ qkv,
     const float* __restrict__ lse, const float* __restrict__ Dbuf, int Tn, int C, int NH) {
-    __shared__ bf16 Ks[KV_TILE * LDR], Kt[HS * LDR], Vs[KV_TILE * LDR];
+    extern __shared__ __attribute__((aligned(16))) bf16 ring[];
+    auto Ks = [&](int i) { return ring + i * TILE_ELEMS; };
+    auto Vs = [&](int i) { return ring + (2 + i) * TILE_ELEMS; };
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, g = lane >> 5;
     const int qt = gridDim.x - 1 - blockIdx.x;
     const int bh = blockIdx.y, b = bh / NH, h = bh % NH;
@@ -291,40 +331,41 @@ __global__ __launch_bounds__(256) void flash_bwd_dq_kernel(
     const float Dq = ql < Tn ? Dbuf[(int64_t)bh * Tn + ql] : 0.f;
     floatx16 dq[2] = {floatx16{}, floatx16{}};
 
-    const int kv_end = min(Tn, (qt + 1) * Q_PER_BLOCK);
-    for (int k0 = 0; k0 < kv_end; k0 += KV_TILE) {
-        __syncthreads();
-        stage64<true, true>(Ks, Kt, base + C, C3, k0, Tn, tid);
-        stage64<true, false>(Vs, nullptr, base + 2 * C, C3, k0, Tn, tid);
-        __syncthreads();
+    const int ntiles = (min(Tn, (qt + 1) * Q_PER_BLOCK) + TILE - 1) / TILE;
+    dma_tile(Ks(0), base + C, C3, 0, Tn, wid, lane);
+    dma_tile(Vs(0), base + 2 * C, C3, 0, Tn, wid, lane);
+    for (int t = 0; t < ntiles; t++) {
+        const int buf = t & 1, k0 = t * TILE;
+        tile_barrier();
+        if (t + 1 < ntiles) {
+            dma_tile(Ks(buf ^ 1), base + C, C3, k0 + TILE, Tn, wid, lane);
+            dma_tile(Vs(buf ^ 1), base + 2 * C, C3, k0 + TILE, Tn, wid, lane);
+        }
         if (k0 > q0 + 31 || q0 >= Tn) continue;
-        floatx16 s[2] = {floatx16{}, floatx16{}}, dp[2] = {floatx16{}, floatx16{}};
+        const bf16* ks = Ks(buf);
+        const bf16* vs = Vs(buf);
 #pragma unroll
-        for (int kt = 0; kt < 2; kt++)
+        for (int kt = 0; kt < 2; kt++) {
+            floatx16 s = floatx16{}, dp = floatx16{};
 #pragma unroll
             for (int kb = 0; kb < 4; kb++) {
-                const int ro = (32 * kt + (lane & 31)) * LDR + kb * 16 + 8 * g;
-                s[kt] = mfma(ld16(Ks + ro), qf[kb], s[kt]);
-                dp[kt] = mfma(ld16(Vs + ro), df[kb], dp[kt]);
+                s = mfma(frag_rows(ks, 32 * kt, kb, lane), qf[kb], s);
+                dp = mfma(frag_rows(vs, 32 * kt, kb, lane), df[kb], dp);
             }
-#pragma unroll
-        for (int kt = 0; kt < 2; kt++)
 #pragma unroll
             for (int v = 0; v < 16; v++) {
                 const int key = k0 + 32 * kt + 8 * (v >> 2) + 4 * g + (v & 3);
-                const float p = (key <= ql && ql < Tn) ? exp2f(s[kt][v] * sc - l2) : 0.f;
-                dp[kt][v] = p * (dp[kt][v] - Dq);
+                const float p = (key <= ql && ql < Tn) ? exp2f(s[v] * sc - l2) : 0.f;
+                dp[v] = p * (dp[v] - Dq);
             }
-#pragma unroll
-        for (int kt = 0; kt < 2; kt++)
 #pragma unroll
             for (int hh = 0; hh < 2; hh++) {
-                const bf16x8 db = half_tile(dp[kt], hh);
-                const int kk = 32 * kt + 16 * hh + 4 * g;
+                const bf16x8 db = half_tile(dp, hh);
 #pragma unroll
                 for (int dt = 0; dt < 2; dt++)
-                    dq[dt] = mfma(ld_runs(Kt + (32 * dt + (lane & 31)) * LDR, kk), db, dq[dt]);
+                    dq[dt] = mfma(frag_dims(ks, 32 * dt, 32 * kt + 16 * hh, lane), db, dq[dt]);
             }
+        }
     }
     if (ql < Tn) {
         bf16* qrow = dqkv + ((int64_t)b * Tn + ql) * C3 + h * HS;
@@ -343,13 +384,15 @@ __global__ __launch_bounds__(256) void flash_bwd_dq_kernel(
 void flash_attention_fwd(bf16* out, float* lse, const bf16* qkv, int B, int Tn, int C, int NH,
                          hipStream_t st) {
     dim3 grid(ceil_div(Tn, Q_PER_BLOCK), B * NH);
-    flash_fwd_kernel<<<grid, 256, 0, st>>>(out, lse, qkv, Tn, C, NH);
+    flash_fwd_kernel<<<grid, 256, 4 * TILE_ELEMS * sizeof(bf16), st>>>(out, lse, qkv, Tn, C, NH);
 }
 
 // Dbuf must already hold D = rowsum(dout * out) per (b, h, t).
 void flash_attention_bwd(bf16* dqkv, const bf16* dout, const bf16* qkv, const float* lse,
                          const float* Dbuf, int B, int Tn, int C, int NH, hipStream_t st) {
     dim3 grid(ceil_div(Tn, Q_PER_BLOCK), B * NH);
-    flash_bwd_dkv_kernel<<<grid, 256, 0, st>>>(dqkv, dout, qkv, lse, Dbuf, Tn, C, NH);
-    flash_bwd_dq_kernel<<<grid, 256, 0, st>>>(dqkv, dout, qkv, lse, Dbuf, Tn, C, NH);
+    flash_bwd_dkv_kernel<<<grid, 256, 4 * TILE_ELEMS * sizeof(bf16) + 4 * TILE * sizeof(float),
+                           st>>>(dqkv, dout, qkv, lse, Dbuf, Tn, C, NH);
+    flash_bwd_dq_kernel<<<grid, 256, 4 * TILE_ELEMS * sizeof(bf16), st>>>(dqkv, dout, qkv, lse,
+                                                                         Dbuf, Tn, C, NH);
 }
