@@ -29,7 +29,30 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(w, T_sample=256):
+def recorded_traffic(cls):
+    """HBM bytes per launch of kernel class `cls` as the FETCH_SIZE / WRITE_SIZE
+    counter passes recorded them, or None when the kernel sources have changed
+    since (the recorded figures no longer describe the kernels that ran)."""
+    from transformer_lm_amd.prof_summary import source_sha
+    path = os.path.join(ROOT, "profiles", "gpt2_124m_bf16_B16_T1024_class_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    sha, rows = None, {}
+    for line in open(path):
+        f = line.split()
+        if not f or f[0].startswith("#"):
+            continue
+        if f[0] == "source_sha256":
+            sha = f[1]
+        elif len(f) == 3:
+            rows[f[0]] = (float(f[1]), float(f[2]))
+    if sha != source_sha() or cls not in rows:
+        return None
+    return {"fetch_bytes": round(rows[cls][0]), "write_bytes": round(rows[cls][1]),
+            "bytes": round(rows[cls][0] + rows[cls][1])}
+
+
+def cpu_baseline(w, T_sample=1024):
     """The oracle (fp64, plain loops, OpenMP over independent outputs) on one
     sequence of T_sample tokens of the same model: one full training step."""
     import oracle
@@ -60,6 +83,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default=WORKLOAD)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after timing, run a plain 1 GiB device copy (reference for the "
+                         "FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -137,10 +163,22 @@ def main():
         achieved = wk / (ms * 1e-3)
         peak = PEAK_HBM_BYTES if isb else PEAK_BF16_FLOPS
         unit_div = 1e9 if isb else 1e12
+        tr = recorded_traffic(dominant) if w.name == WORKLOAD else None
         roofline = {"kernel": dominant, "bound": "hbm" if isb else "mfma",
                     "achieved": round(achieved / unit_div, 2), "peak": peak / unit_div,
                     "unit": "GB/s" if isb else "TFLOP/s", "frac": round(achieved / peak, 4),
-                    "traffic": None, "launches": n, "avg_launch_ms": round(ms / n, 4)}
+                    "traffic": tr["bytes"] if tr else None,
+                    "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-scaled)",
+                    "traffic_fetch_write": [tr["fetch_bytes"], tr["write_bytes"]] if tr else None,
+                    "launches": n, "avg_launch_ms": round(ms / n, 4)}
+
+    if args.calibrate_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:
