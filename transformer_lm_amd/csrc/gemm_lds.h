@@ -1,5 +1,5 @@
 // bf16 matrix products fed by direct global -> LDS loads (gfx950
-// global_load_lds_dwordx4), for the three operand layouts of the linear
+// buffer_load_dwordx4 ... lds), for the three operand layouts of the linear
 // layers, on v_mfma_f32_32x32x16_bf16 with fp32 accumulation:
 //   out[i, j] = sum_p X(i, p) Y(j, p) (+ bias[j]) (+ residual[i, j]).
 //
@@ -51,7 +51,18 @@ __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Buffer resource over the bytes at base (gfx9 raw buffer, no range limit
+// beyond 4 GB offsets; every offset used here stays far below that).
+#if __HIP_DEVICE_COMPILE__
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_at(const void* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, 0x00020000);
+}
+#endif
+
 // One operand tile (ROWS x BK) of the ring: its loads and fragment reads.
+// Loads are MUBUF buffer_load ... lds: unlike the FLAT-encoded global form,
+// they leave the compiler's LDS wait counting exact, so fragment reads can
+// stay in flight across matrix products.
 template <int ROWS, int BK, int NW, bool RC>
 struct LdsOperand {
     static constexpr int CHUNKS = ROWS * BK / 8;  // 16-byte chunks per tile
@@ -60,28 +71,42 @@ struct LdsOperand {
     static constexpr int ELEMS = ROWS * BK;
     static_assert(TOTAL * 64 == CHUNKS, "a tile is a whole number of wave loads");
 
-    // Loads the tile at rows row0.., reduction k0.. into LDS at s. The last
-    // wave may repeat its final chunk so that all waves issue NPW loads.
-    __device__ __forceinline__ static void load(bf16* s, const bf16* __restrict__ g, int ld,
-                                                int nrows, int row0, int k0, int wid, int lane) {
+    uint32_t voff[NPW];  // this lane's byte offset from the tile origin, per load
+
+    // Offsets for the tile whose rows start at row0; rows past the matrix edge
+    // (nrows) read the last row (reduction-contiguous) or the last 8 rows
+    // (row-contiguous), and their results are discarded. The last wave may
+    // repeat its final chunk so that all waves issue NPW loads.
+    __device__ __forceinline__ void init(int ld, int nrows, int row0, int wid, int lane) {
 #pragma unroll
         for (int j = 0; j < NPW; j++) {
-            const int blk = min(wid * NPW + j, TOTAL - 1);
-            const int ch = blk * 64 + lane;
-            const bf16* src;
+            const int ch = min(wid * NPW + j, TOTAL - 1) * 64 + lane;
             if (!RC) {
                 constexpr int CPR = BK / 8;
                 const int r = ch / CPR, lc = (ch % CPR) ^ pc_swz<BK>(ch / CPR);
-                src = g + (int64_t)min(row0 + r, nrows - 1) * ld + k0 + lc * 8;
+                voff[j] = (uint32_t)((min(row0 + r, nrows - 1) - row0) * ld + lc * 8) * 2u;
             } else {
                 constexpr int CPR = ROWS / 8;
                 const int k = ch / CPR, lc = (ch % CPR) ^ rc_swz<ROWS>(ch / CPR);
-                src = g + (int64_t)(k0 + k) * ld + min(row0 + lc * 8, nrows - 8);
+                voff[j] = (uint32_t)(k * ld + min(row0 + lc * 8, nrows - 8) - row0) * 2u;
             }
-            __builtin_amdgcn_global_load_lds(
-                (const void*)src, (__attribute__((address_space(3))) void*)(s + blk * 512), 16, 0,
+        }
+    }
+
+    // Loads the tile at rows row0.., reduction k0.. into LDS at s.
+    __device__ __forceinline__ void load(bf16* s, const bf16* __restrict__ g, int ld, int row0,
+                                         int k0, int wid) const {
+#if __HIP_DEVICE_COMPILE__  // the buffer builtins exist for the device pass only
+        const bf16* base = RC ? g + (int64_t)k0 * ld + row0 : g + (int64_t)row0 * ld + k0;
+        const auto rs = buffer_at(base);
+#pragma unroll
+        for (int j = 0; j < NPW; j++) {
+            const int blk = min(wid * NPW + j, TOTAL - 1);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rs, (__attribute__((address_space(3))) void*)(s + blk * 512), 16, voff[j], 0, 0,
                 0);
         }
+#endif
     }
 
     // MFMA fragment of tile rows r0..r0+31, reduction block kk (16 wide).
@@ -148,11 +173,15 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_lds_kernel(
 #pragma unroll
         for (int b = 0; b < FM; b++) acc[a][b] = floatx16{};
 
+    XO xo;
+    YO yo;
+    xo.init(ldx, M, i0, wid, lane);
+    yo.init(ldy, N, j0, wid, lane);
 #pragma unroll
     for (int s = 0; s < S - 1; s++)
         if (s < nk) {
-            XO::load(Xs + s * XO::ELEMS, X, ldx, M, i0, kbeg + s * BK, wid, lane);
-            YO::load(Ys + s * YO::ELEMS, Y, ldy, N, j0, kbeg + s * BK, wid, lane);
+            xo.load(Xs + s * XO::ELEMS, X, ldx, i0, kbeg + s * BK, wid);
+            yo.load(Ys + s * YO::ELEMS, Y, ldy, j0, kbeg + s * BK, wid);
         }
 
     const bool do_rowsum = rowsum != nullptr && tn == 0 && tid < BM;
@@ -170,8 +199,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_lds_kernel(
         __builtin_amdgcn_s_barrier();
         if (kt + S - 1 < nk) {
             const int sn = (kt + S - 1) % S;
-            XO::load(Xs + sn * XO::ELEMS, X, ldx, M, i0, kbeg + (kt + S - 1) * BK, wid, lane);
-            YO::load(Ys + sn * YO::ELEMS, Y, ldy, N, j0, kbeg + (kt + S - 1) * BK, wid, lane);
+            xo.load(Xs + sn * XO::ELEMS, X, ldx, i0, kbeg + (kt + S - 1) * BK, wid);
+            yo.load(Ys + sn * YO::ELEMS, Y, ldy, j0, kbeg + (kt + S - 1) * BK, wid);
         }
         const bf16* xb = Xs + (kt % S) * XO::ELEMS;
         const bf16* yb = Ys + (kt % S) * YO::ELEMS;
@@ -188,17 +217,29 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_lds_kernel(
         read_frags(0, a[0], b[0]);
 #pragma unroll
         for (int kk = 0; kk < BK / 16; kk++) {
+            // Fragments of step kk+1 are requested before the products of
+            // step kk; the scheduling fences keep the compiler from sinking
+            // each read next to its first use (which would expose the LDS
+            // latency before every product).
             if (kk + 1 < BK / 16) read_frags(kk + 1, a[(kk + 1) & 1], b[(kk + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int fn = 0; fn < FN; fn++)
 #pragma unroll
                 for (int fm = 0; fm < FM; fm++)
                     acc[fn][fm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                         a[kk & 1][fn], b[kk & 1][fm], acc[fn][fm], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
     if (do_rowsum && i0 + tid < M) rowsum[blockIdx.z * rowsum_stride + i0 + tid] = rsum;
     (void)NT;
+    // Pin the accumulators to AGPRs: otherwise the bf16 epilogue's conversions
+    // pull them into VGPRs for the whole kernel, and wide wave tiles spill.
+#pragma unroll
+    for (int fn = 0; fn < FN; fn++)
+#pragma unroll
+        for (int fm = 0; fm < FM; fm++) asm volatile("" : "+a"(acc[fn][fm]));
 
     // epilogue: lane holds column i = l%32 of each tile and rows j in runs of 4
 #pragma unroll

@@ -22,10 +22,15 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(float* __restrict__ o
     *reinterpret_cast<floatx4*>(out + i) = s;
 }
 
+// 128x192 tiles on four waves (64x96 each) with an 80 KB two-stage ring: two
+// blocks share a CU, so one block's barrier and load waits overlap the other's
+// matrix products. 16384-row outputs of width 768, 2304 and 3072 make exactly
+// 1, 3 and 4 rounds of 512 blocks.
 using Cfg = GemmCfg<128, 128, 32, 2, 2, 16>;      // register-staged fallback
-using FwdCfg = GemmLds<256, 192, 64, 4, 2, 8, 2>;  // y = x W^T and dx = dy W
-using DwCfg = GemmLds<128, 128, 64, 2, 2, 8, 2>;   // dW = dy^T x
+using FwdCfg = GemmLds<128, 192, 64, 2, 2, 8, 2>;  // y = x W^T and dx = dy W
+using DwCfg = GemmLds<128, 192, 64, 2, 2, 8, 2>;   // dW = dy^T x
 constexpr int LDS_BK = 64;
+constexpr int BLOCK_SLOTS = 2 * 256;  // resident blocks: two per CU on 256 CUs
 
 // The direct-to-LDS kernels use more than 64 KB of LDS; raise their limits once.
 static void prepare_lds_kernels() {
@@ -63,15 +68,27 @@ void gemm_bf16_bwd_dx(bf16* dinp, const bf16* dout, const bf16* w, int M, int N,
                                     nullptr, 0, st);
 }
 
-// Splits of the B*T reduction of a weight gradient [N, K]: enough blocks to
-// cover the chip about four times over, each split at least 512 rows long.
+// Splits of the B*T reduction of a weight gradient [N, K]. Cost model, in
+// units of one block's time per reduction row: rounds of resident blocks times
+// rows per split, plus the fp32 partials' HBM round trip (8 bytes per output
+// per split, about 8e-5 rows each at HBM speed) and the reduce launch. More
+// splits must win by 5%. At most 16 splits of at least 512 rows.
 static int dw_splits(int M, int N, int K) {
     const int tiles = ceil_div(N, DwCfg::bm) * ceil_div(K, DwCfg::bn);
-    int s = (4 * 256 + tiles - 1) / tiles;
-    const int smax = M / 512;
-    if (s > smax) s = smax;
-    if (s > 16) s = 16;
-    return s < 1 ? 1 : s;
+    int smax = M / 512;
+    if (smax > 16) smax = 16;
+    int best = 1;
+    double best_cost = 0.0;
+    for (int s = 1; s <= (smax < 1 ? 1 : smax); s++) {
+        const double rounds = ceil_div(tiles * s, BLOCK_SLOTS);
+        double cost = rounds * ceil_div(M, s);
+        if (s > 1) cost += 8e-5 * s * (double)N * K + 200.0;
+        if (s == 1 || cost < 0.95 * best_cost) {
+            best_cost = cost;
+            best = s;
+        }
+    }
+    return best;
 }
 
 int64_t gemm_dw_workspace_floats(int M, int N, int K) {

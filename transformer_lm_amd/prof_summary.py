@@ -17,13 +17,10 @@ from collections import defaultdict
 
 # kernel symbol (substring) -> library timing class
 CLASSES = [
-    (r"gemm_(lds|mfma)_kernel<256, 192, 64, 4, 2, 8, 2, false, false", "matmul_fwd"),
-    (r"gemm_(lds|mfma)_kernel<256, 192, 64, 4, 2, 8, 2, false, true", "matmul_bwd_dx"),
-    (r"gemm_(lds|mfma)_kernel<128, 128, 64, 2, 2, 8, 2, true, true", "matmul_bwd_dw"),
+    (r"gemm_(lds|mfma)_kernel<[^>]*false, false", "matmul_fwd"),
+    (r"gemm_(lds|mfma)_kernel<[^>]*false, true", "matmul_bwd_dx"),
+    (r"gemm_(lds|mfma)_kernel<[^>]*true, true", "matmul_bwd_dw"),
     (r"split_reduce_kernel", "matmul_bwd_dw"),
-    (r"gemm_mfma_kernel<128, 128, 32, 2, 2, 16, false, false", "matmul_fwd"),
-    (r"gemm_mfma_kernel<128, 128, 32, 2, 2, 16, false, true", "matmul_bwd_dx"),
-    (r"gemm_mfma_kernel<128, 128, 32, 2, 2, 16, true, true", "matmul_bwd_dw"),
     (r"flash_fwd_kernel|attention_fwd_rows", "attention_fwd"),
     (r"flash_bwd|attention_bwd", "attention_bwd"),
     (r"layernorm_fwd", "layernorm_fwd"),
