@@ -199,7 +199,7 @@ template <typename T>
 void attention_fwd(T* out, float* lse, const T* qkv, int B, int Tn, int C, int NH,
                    hipStream_t st) {
     if constexpr (std::is_same<T, bf16>::value) {
-        if (C / NH == 64) {
+        if (C / NH == 64 && flash_attention_fits(Tn, C)) {
             flash_attention_fwd(out, lse, qkv, B, Tn, C, NH, st);
             return;
         }
@@ -210,17 +210,17 @@ void attention_fwd(T* out, float* lse, const T* qkv, int B, int Tn, int C, int N
 
 template <typename T>
 void attention_bwd(T* dqkv, const T* dout, const T* qkv, const T* out, const float* lse,
-                   float* Dbuf, int B, int Tn, int C, int NH, hipStream_t st) {
-    dim3 grid(ceil_div(Tn, AT_ROWS), B * NH);
-    attention_bwd_d_kernel<T><<<grid, 256, 0, st>>>(Dbuf, dout, out, Tn, C, NH);
+                   float* work, int B, int Tn, int C, int NH, hipStream_t st) {
     if constexpr (std::is_same<T, bf16>::value) {
-        if (C / NH == 64) {
-            flash_attention_bwd(dqkv, dout, qkv, lse, Dbuf, B, Tn, C, NH, st);
+        if (C / NH == 64 && flash_attention_fits(Tn, C)) {
+            flash_attention_bwd(dqkv, dout, qkv, out, lse, work, B, Tn, C, NH, st);
             return;
         }
     }
-    attention_bwd_dq_kernel<T><<<grid, 256, 0, st>>>(dqkv, dout, qkv, lse, Dbuf, Tn, C, NH);
-    attention_bwd_dkv_kernel<T><<<grid, 256, 0, st>>>(dqkv, dout, qkv, lse, Dbuf, Tn, C, NH);
+    dim3 grid(ceil_div(Tn, AT_ROWS), B * NH);
+    attention_bwd_d_kernel<T><<<grid, 256, 0, st>>>(work, dout, out, Tn, C, NH);
+    attention_bwd_dq_kernel<T><<<grid, 256, 0, st>>>(dqkv, dout, qkv, lse, work, Tn, C, NH);
+    attention_bwd_dkv_kernel<T><<<grid, 256, 0, st>>>(dqkv, dout, qkv, lse, work, Tn, C, NH);
 }
 
 template void attention_fwd<float>(float*, float*, const float*, int, int, int, int, hipStream_t);

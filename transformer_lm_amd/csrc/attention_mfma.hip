@@ -25,6 +25,11 @@
 // transpose reads fetch the other operand's rows in that order.
 //
 // Softmax runs in base 2: x = s * log2(e) / sqrt(hs), p = exp2(x - m).
+//
+// Launch bounds ask for 4 (forward), 2 (dK/dV) and 3 (dQ) waves per SIMD:
+// the register budgets that fit keep every kernel free of spills, and the
+// extra waves hide the matrix-core / exponential / LDS latencies of each
+// wave's serial tile loop.
 #include "gemm_lds.h"
 
 #define HS 64
@@ -42,18 +47,31 @@ __device__ __forceinline__ bf16x8 ld16(const bf16* p) { return *reinterpret_cast
 
 __device__ __forceinline__ int tswz(int r) { return pc_swz<64>(r); }
 
-// Direct loads of rows r0..r0+63 of a 64-wide head slice (row stride ld) into
-// the LDS tile s; rows >= nrows repeat row nrows-1. 4 waves, 2 loads each.
-__device__ __forceinline__ void dma_tile(bf16* s, const bf16* __restrict__ g, int64_t ld, int r0,
-                                         int nrows, int wid, int lane) {
+// 2^x on the hardware exponential (no denormal rescaling: probabilities that
+// small do not change a bf16 result).
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Buffer resource over the bytes at base; the launchers keep every offset of
+// one sequence's slice below 2^31.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slice_rsrc(const void* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, 0x00020000);
+}
+
+__device__ __forceinline__ __attribute__((address_space(3))) void* lds_ptr(const void* p) {
+    return (__attribute__((address_space(3))) void*)(p);
+}
+
+// Direct loads (buffer_load ... lds) of rows r0..r0+63 of a 64-wide head slice
+// (row stride ld elements, soff bytes past the resource base) into the LDS tile
+// s; rows >= nrows repeat row nrows-1. 4 waves, 2 loads each.
+__device__ __forceinline__ void dma_tile(bf16* s, __amdgpu_buffer_rsrc_t rs, int soff, int ld,
+                                         int r0, int nrows, int wid, int lane) {
 #pragma unroll
     for (int j = 0; j < 2; j++) {
         const int blk = wid * 2 + j, ch = blk * 64 + lane;
         const int r = ch >> 3, lc = (ch & 7) ^ tswz(ch >> 3);
-        const bf16* src = g + (int64_t)min(r0 + r, nrows - 1) * ld + lc * 8;
-        __builtin_amdgcn_global_load_lds((const void*)src,
-                                         (__attribute__((address_space(3))) void*)(s + blk * 512),
-                                         16, 0, 0);
+        const uint32_t off = (uint32_t)(min(r0 + r, nrows - 1) * ld + lc * 8) * 2u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds_ptr(s + blk * 512), 16, off, soff, 0, 0);
     }
 }
 
@@ -96,8 +114,9 @@ __device__ __forceinline__ void tile_barrier() {
 // ---------------------------------------------------------------- forward --
 // Block: 128 queries of one (b, h); wave w owns queries q0 .. q0+31, lane l the
 // query q0 + l%32. Per 64-key tile: S^T (keys x queries) = K Q^T, online
-// softmax per query, O^T (dims x queries) += V^T P^T.
-__global__ __launch_bounds__(256) void flash_fwd_kernel(bf16* __restrict__ out,
+// softmax per query, O^T (dims x queries) += V^T P^T. Only tiles that cross
+// the causal diagonal or the sequence end are masked.
+__global__ __launch_bounds__(256, 4) void flash_fwd_kernel(bf16* __restrict__ out,
                                                         float* __restrict__ lse,
                                                         const bf16* __restrict__ qkv, int Tn,
                                                         int C, int NH) {
@@ -111,6 +130,7 @@ __global__ __launch_bounds__(256) void flash_fwd_kernel(bf16* __restrict__ out,
     const int bh = blockIdx.y, b = bh / NH, h = bh % NH;
     const int C3 = 3 * C;
     const bf16* base = qkv + (int64_t)b * Tn * C3 + h * HS;
+    const auto rs = slice_rsrc(base);
     const int q0 = qt * Q_PER_BLOCK + wid * 32;
     const int ql = q0 + (lane & 31);
     const float sc = LOG2E / 8.0f;  // log2(e) / sqrt(64)
@@ -123,42 +143,47 @@ __global__ __launch_bounds__(256) void flash_fwd_kernel(bf16* __restrict__ out,
     float m = -INFINITY, l = 0.f;
 
     const int ntiles = (min(Tn, (qt + 1) * Q_PER_BLOCK) + TILE - 1) / TILE;
-    dma_tile(Ks(0), base + C, C3, 0, Tn, wid, lane);
-    dma_tile(Vs(0), base + 2 * C, C3, 0, Tn, wid, lane);
+    dma_tile(Ks(0), rs, 2 * C, C3, 0, Tn, wid, lane);
+    dma_tile(Vs(0), rs, 4 * C, C3, 0, Tn, wid, lane);
     for (int t = 0; t < ntiles; t++) {
         const int buf = t & 1, k0 = t * TILE;
         tile_barrier();
         if (t + 1 < ntiles) {
-            dma_tile(Ks(buf ^ 1), base + C, C3, k0 + TILE, Tn, wid, lane);
-            dma_tile(Vs(buf ^ 1), base + 2 * C, C3, k0 + TILE, Tn, wid, lane);
+            dma_tile(Ks(buf ^ 1), rs, 2 * C, C3, k0 + TILE, Tn, wid, lane);
+            dma_tile(Vs(buf ^ 1), rs, 4 * C, C3, k0 + TILE, Tn, wid, lane);
         }
         if (k0 > q0 + 31 || q0 >= Tn) continue;  // every key of the tile is masked
         const bf16* kt_s = Ks(buf);
         const bf16* vt_s = Vs(buf);
         floatx16 s[2] = {floatx16{}, floatx16{}};
 #pragma unroll
-        for (int kt = 0; kt < 2; kt++)
+        for (int kb = 0; kb < 4; kb++)
 #pragma unroll
-            for (int kb = 0; kb < 4; kb++) s[kt] = mfma(frag_rows(kt_s, 32 * kt, kb, lane), qf[kb], s[kt]);
+            for (int kt = 0; kt < 2; kt++) s[kt] = mfma(frag_rows(kt_s, 32 * kt, kb, lane), qf[kb], s[kt]);
+        if (k0 + TILE - 1 > q0 || k0 + TILE > Tn) {  // wave-uniform
+#pragma unroll
+            for (int kt = 0; kt < 2; kt++)
+#pragma unroll
+                for (int v = 0; v < 16; v++) {
+                    const int key = k0 + 32 * kt + 8 * (v >> 2) + 4 * g + (v & 3);
+                    if (key > ql || key >= Tn) s[kt][v] = -INFINITY;
+                }
+        }
         float mx = -INFINITY;
 #pragma unroll
         for (int kt = 0; kt < 2; kt++)
 #pragma unroll
-            for (int v = 0; v < 16; v++) {
-                const int key = k0 + 32 * kt + 8 * (v >> 2) + 4 * g + (v & 3);
-                const float x = (key <= ql && key < Tn) ? s[kt][v] * sc : -INFINITY;
-                s[kt][v] = x;
-                mx = fmaxf(mx, x);
-            }
+            for (int v = 0; v < 16; v++) mx = fmaxf(mx, s[kt][v]);
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float mn = fmaxf(m, mx);
-        const float corr = exp2f(m - mn);
+        // every processed tile holds a visible key for every lane, so mn is finite
+        const float mn = fmaxf(m, mx * sc);
+        const float corr = exp2_fast(m - mn);
         float ps = 0.f;
 #pragma unroll
         for (int kt = 0; kt < 2; kt++)
 #pragma unroll
             for (int v = 0; v < 16; v++) {
-                const float p = exp2f(s[kt][v] - mn);
+                const float p = exp2_fast(fmaf(s[kt][v], sc, -mn));
                 s[kt][v] = p;
                 ps += p;
             }
@@ -193,14 +218,44 @@ __global__ __launch_bounds__(256) void flash_fwd_kernel(bf16* __restrict__ out,
     }
 }
 
+// ---------------------------------------------------- backward preparation --
+// Per (b, t, h): D = sum_d dO[d] O[d] (the softmax-backward correction of the
+// row) and the log-sum-exp in base 2. Eight lanes per row, 16 bytes each.
+__global__ __launch_bounds__(256) void flash_bwd_prep_kernel(float* __restrict__ Dbuf,
+                                                             float* __restrict__ lse2,
+                                                             const float* __restrict__ lse,
+                                                             const bf16* __restrict__ dout,
+                                                             const bf16* __restrict__ out,
+                                                             int Tn, int NH, int64_t rows) {
+    const int64_t row = (blockIdx.x * (int64_t)blockDim.x + threadIdx.x) >> 3;  // (b*Tn + t)*NH + h
+    const int j = threadIdx.x & 7;
+    float s = 0.f;
+    if (row < rows) {
+        const bf16x8 a = ld16(dout + row * HS + 8 * j);
+        const bf16x8 c = ld16(out + row * HS + 8 * j);
+#pragma unroll
+        for (int i = 0; i < 8; i++) s += (float)a[i] * (float)c[i];
+    }
+    s += __shfl_xor(s, 1, 64);
+    s += __shfl_xor(s, 2, 64);
+    s += __shfl_xor(s, 4, 64);
+    if (row < rows && j == 0) {
+        const int h = (int)(row % NH);
+        const int64_t bt = row / NH, b = bt / Tn, t = bt % Tn;
+        const int64_t i = (b * NH + h) * Tn + t;
+        Dbuf[i] = s;
+        lse2[i] = lse[i] * LOG2E;
+    }
+}
+
 // ------------------------------------------------------------ backward dK dV --
 // Block: 128 keys of one (b, h); wave w owns keys kw .. kw+31, lane l the key
 // kw + l%32. Per 64-query tile (queries >= the block's first key), in two
 // 32-query halves: S = Q K^T and dP = dO V^T (queries x keys),
 // P = exp2(S*c - lse2), dS = P (dP - D); dV^T += dO^T P; dK^T += Q^T dS.
-__global__ __launch_bounds__(256) void flash_bwd_dkv_kernel(
+__global__ __launch_bounds__(256, 2) void flash_bwd_dkv_kernel(
     bf16* __restrict__ dqkv, const bf16* __restrict__ dout, const bf16* __restrict__ qkv,
-    const float* __restrict__ lse, const float* __restrict__ Dbuf, int Tn, int C, int NH) {
+    const float* __restrict__ lse2, const float* __restrict__ Dbuf, int Tn, int C, int NH) {
     extern __shared__ __attribute__((aligned(16))) bf16 ring[];
     auto Qs = [&](int i) { return ring + i * TILE_ELEMS; };
     auto Os = [&](int i) { return ring + (2 + i) * TILE_ELEMS; };
@@ -211,8 +266,9 @@ __global__ __launch_bounds__(256) void flash_bwd_dkv_kernel(
     const int C3 = 3 * C;
     const bf16* base = qkv + (int64_t)b * Tn * C3 + h * HS;
     const bf16* dbase = dout + (int64_t)b * Tn * C + h * HS;
-    const float* lrow = lse + (int64_t)bh * Tn;
-    const float* Drow = Dbuf + (int64_t)bh * Tn;
+    const auto rq = slice_rsrc(base);
+    const auto ro = slice_rsrc(dbase);
+    const auto rl = slice_rsrc(wid == 2 ? lse2 + (int64_t)bh * Tn : Dbuf + (int64_t)bh * Tn);
     const int kb0 = blockIdx.x * Q_PER_BLOCK;
     const int kw = kb0 + wid * 32;
     const int kl = kw + (lane & 31);
@@ -227,16 +283,15 @@ __global__ __launch_bounds__(256) void flash_bwd_dkv_kernel(
     floatx16 dk[2] = {floatx16{}, floatx16{}}, dv[2] = {floatx16{}, floatx16{}};
 
     // tile t covers queries kb0 + 64 t ..; the per-query statistics come along
-    // by direct loads (wave 2: log-sum-exp, wave 3: D), one float per lane
+    // by direct loads (wave 2: base-2 log-sum-exp, wave 3: D), one float a lane
     auto issue = [&](int t, int buf) {
         const int q0 = kb0 + t * TILE;
-        dma_tile(Qs(buf), base, C3, q0, Tn, wid, lane);
-        dma_tile(Os(buf), dbase, C, q0, Tn, wid, lane);
+        dma_tile(Qs(buf), rq, 0, C3, q0, Tn, wid, lane);
+        dma_tile(Os(buf), ro, 0, C, q0, Tn, wid, lane);
         if (wid >= 2) {
-            const float* src = (wid == 2 ? lrow : Drow) + min(q0 + lane, Tn - 1);
-            float* dst = wid == 2 ? ls(buf) : Ds(buf);
-            __builtin_amdgcn_global_load_lds((const void*)src,
-                                             (__attribute__((address_space(3))) void*)dst, 4, 0, 0);
+            const uint32_t off = (uint32_t)min(q0 + lane, Tn - 1) * 4u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, lds_ptr(wid == 2 ? ls(buf) : Ds(buf)), 4,
+                                                     off, 0, 0, 0);
         }
     };
     const int ntiles = (Tn - kb0 + TILE - 1) / TILE;
@@ -246,6 +301,7 @@ __global__ __launch_bounds__(256) void flash_bwd_dkv_kernel(
         tile_barrier();
         if (t + 1 < ntiles) issue(t + 1, buf ^ 1);
         if (kw > q0 + TILE - 1 || kw >= Tn) continue;  // no query of the tile sees these keys
+        const bool edge = q0 < kw + 31 || q0 + TILE > Tn;  // wave-uniform
         const bf16* qs = Qs(buf);
         const bf16* os = Os(buf);
 #pragma unroll
@@ -263,9 +319,12 @@ __global__ __launch_bounds__(256) void flash_bwd_dkv_kernel(
                 const floatx4 d4 = *reinterpret_cast<const floatx4*>(&Ds(buf)[qo]);
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
-                    const int q = q0 + qo + e, v = 4 * r + e;
-                    const float p =
-                        (kl <= q && q < Tn) ? exp2f(s[v] * sc - l4[e] * LOG2E) : 0.f;
+                    const int v = 4 * r + e;
+                    float p = exp2_fast(fmaf(s[v], sc, -l4[e]));
+                    if (edge) {
+                        const int q = q0 + qo + e;
+                        p = (kl <= q && q < Tn) ? p : 0.f;
+                    }
                     s[v] = p;
                     dp[v] = p * (dp[v] - d4[e]);
                 }
@@ -305,9 +364,9 @@ __global__ __launch_bounds__(256) void flash_bwd_dkv_kernel(
 // Block: 128 queries; wave w owns queries q0 .. q0+31, lane l the query
 // q0 + l%32. Per 64-key tile: S^T = K Q^T, dP^T = V dO^T (keys x queries),
 // dS^T = P^T (dP^T - D); dQ^T += K^T dS^T.
-__global__ __launch_bounds__(256) void flash_bwd_dq_kernel(
+__global__ __launch_bounds__(256, 3) void flash_bwd_dq_kernel(
     bf16* __restrict__ dqkv, const bf16* __restrict__ dout, const bf16* __restrict__ qkv,
-    const float* __restrict__ lse, const float* __restrict__ Dbuf, int Tn, int C, int NH) {
+    const float* __restrict__ lse2, const float* __restrict__ Dbuf, int Tn, int C, int NH) {
     extern __shared__ __attribute__((aligned(16))) bf16 ring[];
     auto Ks = [&](int i) { return ring + i * TILE_ELEMS; };
     auto Vs = [&](int i) { return ring + (2 + i) * TILE_ELEMS; };
@@ -316,6 +375,7 @@ __global__ __launch_bounds__(256) void flash_bwd_dq_kernel(
     const int bh = blockIdx.y, b = bh / NH, h = bh % NH;
     const int C3 = 3 * C;
     const bf16* base = qkv + (int64_t)b * Tn * C3 + h * HS;
+    const auto rs = slice_rsrc(base);
     const int q0 = qt * Q_PER_BLOCK + wid * 32;
     const int ql = q0 + (lane & 31);
     const float sc = LOG2E / 8.0f;
@@ -327,21 +387,22 @@ __global__ __launch_bounds__(256) void flash_bwd_dq_kernel(
         df[kb] = ql < Tn ? ld16(dout + ((int64_t)b * Tn + ql) * C + h * HS + kb * 16 + 8 * g)
                          : bf16x8{};
     }
-    const float l2 = ql < Tn ? lse[(int64_t)bh * Tn + ql] * LOG2E : 0.f;
+    const float l2 = ql < Tn ? lse2[(int64_t)bh * Tn + ql] : 0.f;
     const float Dq = ql < Tn ? Dbuf[(int64_t)bh * Tn + ql] : 0.f;
     floatx16 dq[2] = {floatx16{}, floatx16{}};
 
     const int ntiles = (min(Tn, (qt + 1) * Q_PER_BLOCK) + TILE - 1) / TILE;
-    dma_tile(Ks(0), base + C, C3, 0, Tn, wid, lane);
-    dma_tile(Vs(0), base + 2 * C, C3, 0, Tn, wid, lane);
+    dma_tile(Ks(0), rs, 2 * C, C3, 0, Tn, wid, lane);
+    dma_tile(Vs(0), rs, 4 * C, C3, 0, Tn, wid, lane);
     for (int t = 0; t < ntiles; t++) {
         const int buf = t & 1, k0 = t * TILE;
         tile_barrier();
         if (t + 1 < ntiles) {
-            dma_tile(Ks(buf ^ 1), base + C, C3, k0 + TILE, Tn, wid, lane);
-            dma_tile(Vs(buf ^ 1), base + 2 * C, C3, k0 + TILE, Tn, wid, lane);
+            dma_tile(Ks(buf ^ 1), rs, 2 * C, C3, k0 + TILE, Tn, wid, lane);
+            dma_tile(Vs(buf ^ 1), rs, 4 * C, C3, k0 + TILE, Tn, wid, lane);
         }
         if (k0 > q0 + 31 || q0 >= Tn) continue;
+        const bool edge = k0 + TILE - 1 > q0 || k0 + TILE > Tn;  // wave-uniform
         const bf16* ks = Ks(buf);
         const bf16* vs = Vs(buf);
 #pragma unroll
@@ -354,8 +415,11 @@ __global__ __launch_bounds__(256) void flash_bwd_dq_kernel(
             }
 #pragma unroll
             for (int v = 0; v < 16; v++) {
-                const int key = k0 + 32 * kt + 8 * (v >> 2) + 4 * g + (v & 3);
-                const float p = (key <= ql && ql < Tn) ? exp2f(s[v] * sc - l2) : 0.f;
+                float p = exp2_fast(fmaf(s[v], sc, -l2));
+                if (edge) {
+                    const int key = k0 + 32 * kt + 8 * (v >> 2) + 4 * g + (v & 3);
+                    p = (key <= ql && key < Tn) ? p : 0.f;
+                }
                 dp[v] = p * (dp[v] - Dq);
             }
 #pragma unroll
@@ -381,18 +445,28 @@ __global__ __launch_bounds__(256) void flash_bwd_dq_kernel(
     }
 }
 
+// The flash kernels address one sequence's qkv slice with 32-bit buffer
+// offsets.
+bool flash_attention_fits(int Tn, int C) { return (int64_t)Tn * 3 * C * 2 < (int64_t(1) << 31); }
+
 void flash_attention_fwd(bf16* out, float* lse, const bf16* qkv, int B, int Tn, int C, int NH,
                          hipStream_t st) {
     dim3 grid(ceil_div(Tn, Q_PER_BLOCK), B * NH);
     flash_fwd_kernel<<<grid, 256, 4 * TILE_ELEMS * sizeof(bf16), st>>>(out, lse, qkv, Tn, C, NH);
 }
 
-// Dbuf must already hold D = rowsum(dout * out) per (b, h, t).
-void flash_attention_bwd(bf16* dqkv, const bf16* dout, const bf16* qkv, const float* lse,
-                         const float* Dbuf, int B, int Tn, int C, int NH, hipStream_t st) {
+// work: 2 * B*NH*Tn floats (D, then the base-2 log-sum-exp).
+void flash_attention_bwd(bf16* dqkv, const bf16* dout, const bf16* qkv, const bf16* out,
+                         const float* lse, float* work, int B, int Tn, int C, int NH,
+                         hipStream_t st) {
+    const int64_t rows = (int64_t)B * Tn * NH;
+    float* Dbuf = work;
+    float* lse2 = work + rows;
+    flash_bwd_prep_kernel<<<(unsigned)ceil_div(rows * 8, 256), 256, 0, st>>>(Dbuf, lse2, lse, dout,
+                                                                           out, Tn, NH, rows);
     dim3 grid(ceil_div(Tn, Q_PER_BLOCK), B * NH);
     flash_bwd_dkv_kernel<<<grid, 256, 4 * TILE_ELEMS * sizeof(bf16) + 4 * TILE * sizeof(float),
-                           st>>>(dqkv, dout, qkv, lse, Dbuf, Tn, C, NH);
-    flash_bwd_dq_kernel<<<grid, 256, 4 * TILE_ELEMS * sizeof(bf16), st>>>(dqkv, dout, qkv, lse,
+                           st>>>(dqkv, dout, qkv, lse2, Dbuf, Tn, C, NH);
+    flash_bwd_dq_kernel<<<grid, 256, 4 * TILE_ELEMS * sizeof(bf16), st>>>(dqkv, dout, qkv, lse2,
                                                                          Dbuf, Tn, C, NH);
 }

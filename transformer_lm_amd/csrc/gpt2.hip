@@ -136,7 +136,7 @@ void plan(const gpt2_config* c, Layout* lay) {
     a[W_DRES] = a[W_DC] = BT * C * es;
     a[W_D3C] = BT * 3 * C * es;
     a[W_D4C] = BT * 4 * C * es;
-    a[W_ATT_D] = B * NH * T * 4;
+    a[W_ATT_D] = 2 * B * NH * T * 4;  // D, then the base-2 log-sum-exp
     a[W_LN_PART] = layernorm_bwd_partials((int)C) * 4;
     a[W_BIAS_PART] = bias_bwd_partials((int)BT, (int)(4 * C)) * 4;
     a[W_ENC_COUNT] = a[W_ENC_CURSOR] = V * 4;

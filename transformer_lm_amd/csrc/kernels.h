@@ -65,15 +65,19 @@ template <typename T>
 void attention_fwd(T* out, float* lse, const T* qkv, int B, int Tn, int C, int NH,
                    hipStream_t st);
 // dqkv (B,T,3C) written; Dbuf: fp32 workspace (B,NH,T).
+// work: 2 * B * NH * Tn floats.
 template <typename T>
 void attention_bwd(T* dqkv, const T* dout, const T* qkv, const T* out, const float* lse,
-                   float* Dbuf, int B, int Tn, int C, int NH, hipStream_t st);
+                   float* work, int B, int Tn, int C, int NH, hipStream_t st);
 
-// the bf16 matrix-core kernels for head size 64 behind the two entry points above
+// the bf16 matrix-core kernels for head size 64 behind the two entry points
+// above, used when flash_attention_fits(Tn, C)
+bool flash_attention_fits(int Tn, int C);
 void flash_attention_fwd(bf16* out, float* lse, const bf16* qkv, int B, int Tn, int C, int NH,
                          hipStream_t st);
-void flash_attention_bwd(bf16* dqkv, const bf16* dout, const bf16* qkv, const float* lse,
-                         const float* Dbuf, int B, int Tn, int C, int NH, hipStream_t st);
+void flash_attention_bwd(bf16* dqkv, const bf16* dout, const bf16* qkv, const bf16* out,
+                         const float* lse, float* work, int B, int Tn, int C, int NH,
+                         hipStream_t st);
 
 // ---- elementwise --------------------------------------------------------------
 template <typename T>
