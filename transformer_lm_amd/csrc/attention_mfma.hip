@@ -103,6 +103,15 @@ __device__ __forceinline__ bf16x8 half_tile(const floatx16& a, int hh) {
     return r;
 }
 
+// One-dimensional grids over (row block, b*h), ordered by decreasing causal
+// work: all heads' last row blocks first. The dispatcher hands out blocks in
+// index order, so long blocks start early and short ones fill in behind them.
+__device__ __forceinline__ void longest_first(int& rb, int& bh, int nrb, int nblocks) {
+    const int nbh = nblocks / nrb;
+    rb = nrb - 1 - (int)blockIdx.x / nbh;
+    bh = (int)blockIdx.x % nbh;
+}
+
 // The next tile may be requested once every wave has finished reading the
 // buffer it refills; the current one is usable once this wave's loads landed
 // and all waves passed the barrier.
@@ -126,8 +135,9 @@ __global__ __launch_bounds__(256, 4) void flash_fwd_kernel(bf16* __restrict__ ou
     auto Ks = [&](int i) { return ring + i * TILE_ELEMS; };
     auto Vs = [&](int i) { return ring + (2 + i) * TILE_ELEMS; };
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, g = lane >> 5;
-    const int qt = gridDim.x - 1 - blockIdx.x;  // longest rows first
-    const int bh = blockIdx.y, b = bh / NH, h = bh % NH;
+    int qt, bh;
+    longest_first(qt, bh, (Tn + Q_PER_BLOCK - 1) / Q_PER_BLOCK, gridDim.x);
+    const int b = bh / NH, h = bh % NH;
     const int C3 = 3 * C;
     const bf16* base = qkv + (int64_t)b * Tn * C3 + h * HS;
     const auto rs = slice_rsrc(base);
@@ -262,14 +272,17 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkv_kernel(
     auto ls = [&](int i) { return reinterpret_cast<float*>(ring + 4 * TILE_ELEMS) + i * TILE; };
     auto Ds = [&](int i) { return reinterpret_cast<float*>(ring + 4 * TILE_ELEMS) + (2 + i) * TILE; };
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, g = lane >> 5;
-    const int bh = blockIdx.y, b = bh / NH, h = bh % NH;
+    int kq, bh;
+    longest_first(kq, bh, (Tn + Q_PER_BLOCK - 1) / Q_PER_BLOCK, gridDim.x);
+    kq = (Tn + Q_PER_BLOCK - 1) / Q_PER_BLOCK - 1 - kq;  // key block 0 has the most queries
+    const int b = bh / NH, h = bh % NH;
     const int C3 = 3 * C;
     const bf16* base = qkv + (int64_t)b * Tn * C3 + h * HS;
     const bf16* dbase = dout + (int64_t)b * Tn * C + h * HS;
     const auto rq = slice_rsrc(base);
     const auto ro = slice_rsrc(dbase);
     const auto rl = slice_rsrc(wid == 2 ? lse2 + (int64_t)bh * Tn : Dbuf + (int64_t)bh * Tn);
-    const int kb0 = blockIdx.x * Q_PER_BLOCK;
+    const int kb0 = kq * Q_PER_BLOCK;
     const int kw = kb0 + wid * 32;
     const int kl = kw + (lane & 31);
     const float sc = LOG2E / 8.0f;
@@ -371,8 +384,9 @@ __global__ __launch_bounds__(256, 3) void flash_bwd_dq_kernel(
     auto Ks = [&](int i) { return ring + i * TILE_ELEMS; };
     auto Vs = [&](int i) { return ring + (2 + i) * TILE_ELEMS; };
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, g = lane >> 5;
-    const int qt = gridDim.x - 1 - blockIdx.x;
-    const int bh = blockIdx.y, b = bh / NH, h = bh % NH;
+    int qt, bh;
+    longest_first(qt, bh, (Tn + Q_PER_BLOCK - 1) / Q_PER_BLOCK, gridDim.x);
+    const int b = bh / NH, h = bh % NH;
     const int C3 = 3 * C;
     const bf16* base = qkv + (int64_t)b * Tn * C3 + h * HS;
     const auto rs = slice_rsrc(base);
@@ -451,7 +465,7 @@ bool flash_attention_fits(int Tn, int C) { return (int64_t)Tn * 3 * C * 2 < (int
 
 void flash_attention_fwd(bf16* out, float* lse, const bf16* qkv, int B, int Tn, int C, int NH,
                          hipStream_t st) {
-    dim3 grid(ceil_div(Tn, Q_PER_BLOCK), B * NH);
+    const dim3 grid(ceil_div(Tn, Q_PER_BLOCK) * B * NH);
     flash_fwd_kernel<<<grid, 256, 4 * TILE_ELEMS * sizeof(bf16), st>>>(out, lse, qkv, Tn, C, NH);
 }
 
@@ -464,7 +478,7 @@ void flash_attention_bwd(bf16* dqkv, const bf16* dout, const bf16* qkv, const bf
     float* lse2 = work + rows;
     flash_bwd_prep_kernel<<<(unsigned)ceil_div(rows * 8, 256), 256, 0, st>>>(Dbuf, lse2, lse, dout,
                                                                            out, Tn, NH, rows);
-    dim3 grid(ceil_div(Tn, Q_PER_BLOCK), B * NH);
+    const dim3 grid(ceil_div(Tn, Q_PER_BLOCK) * B * NH);
     flash_bwd_dkv_kernel<<<grid, 256, 4 * TILE_ELEMS * sizeof(bf16) + 4 * TILE * sizeof(float),
                            st>>>(dqkv, dout, qkv, lse2, Dbuf, Tn, C, NH);
     flash_bwd_dq_kernel<<<grid, 256, 4 * TILE_ELEMS * sizeof(bf16), st>>>(dqkv, dout, qkv, lse2,
