@@ -45,7 +45,13 @@ __device__ __forceinline__ floatx16 mfma(bf16x8 a, bf16x8 b, floatx16 c) {
 
 __device__ __forceinline__ bf16x8 ld16(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
-__device__ __forceinline__ int tswz(int r) { return pc_swz<64>(r); }
+// Chunk permutation of tile row r (8 chunks of 16 bytes, 128-byte rows, so
+// even and odd rows sit on opposite halves of the 256-byte bank line). Row
+// fragments read one chunk of 16 consecutive rows per 16 lanes: the 8 rows of
+// each parity take 8 distinct chunks. Transpose fragments read 4 chunks of 4
+// consecutive rows per 32 lanes: rows r and r+2 (same half) take opposite
+// 4-chunk groups. Both reads are then free of bank conflicts.
+__device__ __forceinline__ int tswz(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
 
 // 2^x on the hardware exponential (no denormal rescaling: probabilities that
 // small do not change a bf16 result).

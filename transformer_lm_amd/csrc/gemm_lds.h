@@ -37,12 +37,18 @@ __device__ __forceinline__ int pc_swz(int r) {
     else return (r >> 2) & 3;  // BK == 32
 }
 
-// chunk permutation of a row-contiguous LDS row k (ROWS elements): even
-// values, so the 32-byte runs read by the transpose loads stay whole
+// chunk permutation of a row-contiguous LDS row k (ROWS elements). One half
+// of a transpose-read fragment load reads 64 bytes at the same logical
+// columns of rows k0..k0+3 (k0 % 4 == 0); the permutation moves whole 64-byte
+// groups (multiples of 4 chunks) so those four land on distinct quarters of
+// the 256-byte bank line: rows that start on the line's first byte cycle
+// through all four quarters, rows that alternate between its halves take the
+// two quarters of their half.
 template <int ROWS>
 __device__ __forceinline__ int rc_swz(int k) {
-    if constexpr ((ROWS * 2) % 256 == 0) return 2 * (k & 3);
-    else return 2 * ((k >> 1) & 1);  // rows 128 bytes off a 256-byte bank line
+    static_assert(ROWS % 64 == 0, "row-contiguous tiles are whole 128-byte multiples");
+    if constexpr (ROWS % 128 == 0) return 4 * (k & 3);
+    else return 4 * ((k >> 1) & 1);
 }
 
 template <int N>
