@@ -22,8 +22,9 @@
 // (a __syncthreads() would also drain the later stages' loads).
 //
 // Requirements: the reduction length is a multiple of BK (each split's too);
-// row counts of row-contiguous operands are multiples of 8. Rows past the
-// matrix edge are fetched from clamped addresses and their outputs discarded.
+// row counts of row-contiguous operands, the output width and its row stride
+// are multiples of 8. Rows past the matrix edge are fetched from clamped
+// addresses and their outputs discarded.
 #pragma once
 
 #include "gemm_mfma.h"
@@ -247,44 +248,69 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_lds_kernel(
 #pragma unroll
         for (int fm = 0; fm < FM; fm++) asm volatile("" : "+a"(acc[fn][fm]));
 
-    // epilogue: lane holds column i = l%32 of each tile and rows j in runs of 4
+    // Epilogue through LDS, one 32-column slice of the wave tile at a time: a
+    // lane holds output row i = l%32 of each 32x32 tile and columns in runs of
+    // 4, so direct stores would write 16 bytes to 32 rows per instruction.
+    // Staged as fp32 rows, the slice leaves as 64-byte (bf16) or 128-byte
+    // (fp32) contiguous row segments; bias and residual are read the same way
+    // and added in fp32 before the single rounding.
+    constexpr int SP = 36;  // staged row stride in floats (32 + 4: spreads banks)
+    static_assert(NW * TM * SP * 4 <= S * (BM + BN) * BK * 2, "staging fits in the ring");
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();  // every wave is done reading the ring
+    float* stage = reinterpret_cast<float*>(lds_ring) + wid * (TM * SP);
+    const int ib = i0 + wm * TM;
 #pragma unroll
-    for (int fn = 0; fn < FN; fn++)
+    for (int fn = 0; fn < FN; fn++) {
 #pragma unroll
-        for (int fm = 0; fm < FM; fm++) {
-            const int i = i0 + wm * TM + fm * 32 + fr;
-            if (i >= M) continue;
+        for (int fm = 0; fm < FM; fm++)
 #pragma unroll
-            for (int q = 0; q < 4; q++) {
-                const int j = j0 + wn * TN + fn * 32 + 8 * q + 4 * g;
-                if (j >= N) continue;
-                float v0 = acc[fn][fm][4 * q], v1 = acc[fn][fm][4 * q + 1];
-                float v2 = acc[fn][fm][4 * q + 2], v3 = acc[fn][fm][4 * q + 3];
-                if (EPI == EPI_F32) {
-                    float* o = reinterpret_cast<float*>(out_) + blockIdx.z * split_stride +
-                               (int64_t)i * ldo + j;
-                    *reinterpret_cast<floatx4*>(o) = floatx4{v0, v1, v2, v3};
-                } else {
+            for (int q = 0; q < 4; q++)
+                *reinterpret_cast<floatx4*>(stage + (fm * 32 + fr) * SP + 8 * q + 4 * g) =
+                    floatx4{acc[fn][fm][4 * q], acc[fn][fm][4 * q + 1], acc[fn][fm][4 * q + 2],
+                            acc[fn][fm][4 * q + 3]};
+        // a wave's LDS accesses are processed in order: its reads below see
+        // these writes, and the next slice's writes follow these reads
+        const int jb = j0 + wn * TN + fn * 32;
+        if (EPI == EPI_F32) {
+#pragma unroll
+            for (int it = 0; it < TM * 8 / 64; it++) {
+                const int idx = it * 64 + lane, r = idx >> 3, c = (idx & 7) * 4;
+                const int i = ib + r, j = jb + c;
+                if (i < M && j < N)
+                    *reinterpret_cast<floatx4*>(reinterpret_cast<float*>(out_) +
+                                                blockIdx.z * split_stride + (int64_t)i * ldo + j) =
+                        *reinterpret_cast<const floatx4*>(stage + r * SP + c);
+            }
+        } else {
+#pragma unroll
+            for (int it = 0; it < TM * 4 / 64; it++) {
+                const int idx = it * 64 + lane, r = idx >> 2, c = (idx & 3) * 8;
+                const int i = ib + r, j = jb + c;
+                if (i < M && j < N) {
+                    const floatx4 lo = *reinterpret_cast<const floatx4*>(stage + r * SP + c);
+                    const floatx4 hi = *reinterpret_cast<const floatx4*>(stage + r * SP + c + 4);
+                    float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
                     if (bias) {
-                        const bf16x4 bv = *reinterpret_cast<const bf16x4*>(bias + j);
-                        v0 += (float)bv[0];
-                        v1 += (float)bv[1];
-                        v2 += (float)bv[2];
-                        v3 += (float)bv[3];
+                        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(bias + j);
+#pragma unroll
+                        for (int e = 0; e < 8; e++) v[e] += (float)bv[e];
                     }
                     if (residual) {
-                        const bf16x4 rv =
-                            *reinterpret_cast<const bf16x4*>(residual + (int64_t)i * ldo + j);
-                        v0 += (float)rv[0];
-                        v1 += (float)rv[1];
-                        v2 += (float)rv[2];
-                        v3 += (float)rv[3];
+                        const bf16x8 rv =
+                            *reinterpret_cast<const bf16x8*>(residual + (int64_t)i * ldo + j);
+#pragma unroll
+                        for (int e = 0; e < 8; e++) v[e] += (float)rv[e];
                     }
-                    *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(out_) + (int64_t)i * ldo + j) =
-                        bf16x4{(bf16)v0, (bf16)v1, (bf16)v2, (bf16)v3};
+                    bf16x8 o;
+#pragma unroll
+                    for (int e = 0; e < 8; e++) o[e] = (bf16)v[e];
+                    *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(out_) + (int64_t)i * ldo +
+                                               j) = o;
                 }
             }
         }
+    }
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int GM, int S>
