@@ -51,129 +51,302 @@ __global__ __launch_bounds__(256) void encoder_bwd_wpe_kernel(float* __restrict_
     dwpe[idx] = s;
 }
 
-__global__ __launch_bounds__(256) void token_count_kernel(const int32_t* __restrict__ tok,
-                                                          int n, int Vp, int* count) {
-    int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) {
-        int id = tok[i];
-        if (id >= 0 && id < Vp) atomicAdd(&count[id], 1);
-    }
+// ---- dwte: a stable counting sort of the positions by token, then segmented
+// sums over the sorted order.
+//
+// Positions are cut into chunks of ENC_CHUNK. For chunk c and token v,
+// count[v][c] = number of positions of v in c; each position's rank among the
+// positions of its token inside its chunk comes from a pairwise count in LDS.
+// The exclusive scan of count in (v, c) order gives every (v, c) its first slot
+// in the sorted order, so slot = scan[v][c] + rank lists each token's positions
+// in increasing order. The sorted order is then cut into ranges of ENC_RANGE
+// slots: a block sums each token segment inside its range in slot order. A
+// segment that lies inside one range is added to dwte at once; one that
+// crosses ranges leaves its per-range pieces (the piece where it starts, and
+// the first piece of every later range it covers) for a fix-up block, which
+// adds them in range order. Every dwte row is written by exactly one block and
+// summed in a fixed order, so the result does not depend on scheduling.
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+#define ENC_CHUNK 1024
+#define ENC_SCAN 4096  // elements per scan block (1024 threads x 4)
+#define ENC_RANGE 32
+
+struct EncWs {
+    int* scan;     // [Vp * nch] counts, then their per-block exclusive scan
+    int* bsum;     // [nsb + 1] scan-block totals, then their exclusive scan (+ total)
+    int* rank;     // [BT] rank of each position within its (token, chunk)
+    int* sorted;   // [BT] positions in (token, position) order
+    float* piece;  // [nr][2][C] head / tail pieces of crossing segments
+    int nch, nsb, nr;
+};
+
+// Carves the workspace (256-byte aligned pieces); with ws == nullptr it only
+// measures, returning the size through *bytes.
+static EncWs enc_ws(void* ws, int BT, int Vp, int C, int64_t* bytes = nullptr) {
+    EncWs w;
+    w.nch = ceil_div(BT, ENC_CHUNK);
+    const int64_t ncount = (int64_t)Vp * w.nch;
+    w.nsb = ceil_div(ncount, ENC_SCAN);
+    w.nr = ceil_div(BT, ENC_RANGE);
+    int64_t off = 0;
+    auto take = [&](int64_t n) {
+        char* r = ws ? (char*)ws + off : nullptr;
+        off += (n + 255) / 256 * 256;
+        return r;
+    };
+    w.scan = (int*)take(ncount * 4);
+    w.bsum = (int*)take((int64_t)(w.nsb + 1) * 4);
+    w.rank = (int*)take((int64_t)BT * 4);
+    w.sorted = (int*)take((int64_t)BT * 4);
+    w.piece = (float*)take((int64_t)w.nr * 2 * C * 4);
+    if (bytes) *bytes = off;
+    return w;
 }
 
-// Exclusive scan of count[0..Vp) into offset[0..Vp] by one 1024-thread block:
-// each thread scans a contiguous slice, then slice totals are scanned in LDS.
-__global__ __launch_bounds__(1024) void token_scan_kernel(const int* __restrict__ count, int Vp,
-                                                          int* __restrict__ offset,
-                                                          int* __restrict__ cursor) {
-    __shared__ int tot[1024];
-    const int tid = threadIdx.x;
-    const int per = (Vp + 1023) / 1024;
-    const int s0 = tid * per, s1 = min(Vp, s0 + per);
-    int s = 0;
-    for (int i = s0; i < s1; i++) s += count[i];
-    tot[tid] = s;
+int64_t encoder_bwd_workspace_bytes(int BT, int Vp, int C) {
+    int64_t bytes = 0;
+    enc_ws(nullptr, BT, Vp, C, &bytes);
+    return bytes;
+}
+
+// One block per chunk: ranks inside the chunk and the chunk's token counts
+// (written by the last position of each token in the chunk).
+__global__ __launch_bounds__(1024) void enc_rank_kernel(const int32_t* __restrict__ tok, int BT,
+                                                        int Vp, int nch, int* __restrict__ count,
+                                                        int* __restrict__ rank) {
+    __shared__ int sh[ENC_CHUNK];
+    const int c = blockIdx.x, tid = threadIdx.x;
+    const int p0 = c * ENC_CHUNK, n = min(ENC_CHUNK, BT - p0);
+    int v = -1;
+    if (tid < n) {
+        v = tok[p0 + tid];
+        if (v < 0 || v >= Vp) v = -1;
+    }
+    sh[tid] = v;
     __syncthreads();
-    if (tid == 0) {
-        int run = 0;
-        for (int i = 0; i < 1024; i++) {
-            int c = tot[i];
-            tot[i] = run;
-            run += c;
+    if (v < 0) return;
+    int before = 0, after = 0;
+    for (int q = 0; q < n; q++) {
+        const int u = sh[q];
+        before += (u == v) & (q < tid);
+        after += (u == v) & (q > tid);
+    }
+    rank[p0 + tid] = before;
+    if (after == 0) count[(int64_t)v * nch + c] = before + 1;
+}
+
+// Exclusive scan of 1024 per-thread values across the block; returns this
+// thread's prefix, and the block total through *total.
+__device__ __forceinline__ int block_exclusive_scan(int x, int* lds, int* total) {
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    int incl = x;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += y;
+    }
+    if (lane == 63) lds[wid] = incl;
+    __syncthreads();
+    if (wid == 0) {
+        int w = lane < 16 ? lds[lane] : 0;
+        int wi = w;
+#pragma unroll
+        for (int d = 1; d < 16; d <<= 1) {
+            const int y = __shfl_up(wi, d, 64);
+            if (lane >= d) wi += y;
         }
-        offset[Vp] = run;
+        if (lane < 16) lds[16 + lane] = wi - w;
+        if (lane == 15) lds[32] = wi;
     }
     __syncthreads();
-    int run = tot[tid];
+    const int r = lds[16 + wid] + incl - x;
+    *total = lds[32];
+    return r;
+}
+
+// Per-block exclusive scan of ENC_SCAN elements in place; block totals to bsum.
+__global__ __launch_bounds__(1024) void enc_scan_block_kernel(int* __restrict__ a, int64_t n,
+                                                              int* __restrict__ bsum) {
+    __shared__ int lds[40];
+    const int64_t base = (int64_t)blockIdx.x * ENC_SCAN + threadIdx.x * 4;
+    int v[4];
+#pragma unroll
+    for (int k = 0; k < 4; k++) v[k] = base + k < n ? a[base + k] : 0;
+    const int t = v[0] + v[1] + v[2] + v[3];
+    int total;
+    int run = block_exclusive_scan(t, lds, &total);
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        if (base + k < n) a[base + k] = run;
+        run += v[k];
+    }
+    if (threadIdx.x == 0) bsum[blockIdx.x] = total;
+}
+
+// Exclusive scan of the nsb block totals by one block; bsum[nsb] = total.
+__global__ __launch_bounds__(1024) void enc_scan_totals_kernel(int* __restrict__ bsum, int nsb) {
+    __shared__ int lds[40];
+    const int per = (nsb + 1023) / 1024;
+    const int s0 = threadIdx.x * per, s1 = min(nsb, s0 + per);
+    int t = 0;
+    for (int i = s0; i < s1; i++) t += bsum[i];
+    int total;
+    int run = block_exclusive_scan(t, lds, &total);
+    __syncthreads();  // every thread has read its totals before any is overwritten
     for (int i = s0; i < s1; i++) {
-        offset[i] = run;
-        cursor[i] = 0;
-        run += count[i];
+        const int x = bsum[i];
+        bsum[i] = run;
+        run += x;
     }
+    if (threadIdx.x == 0) bsum[nsb] = total;
 }
 
-// Buckets positions by token (the order inside a bucket is arbitrary here; the
-// summation kernel below imposes increasing position order).
-__global__ __launch_bounds__(256) void token_fill_kernel(const int32_t* __restrict__ tok, int n,
-                                                         int Vp, const int* __restrict__ offset,
-                                                         int* cursor, int* __restrict__ bucket) {
-    int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) {
-        int id = tok[i];
-        if (id >= 0 && id < Vp) bucket[offset[id] + atomicAdd(&cursor[id], 1)] = i;
-    }
+__global__ __launch_bounds__(256) void enc_fill_kernel(const int32_t* __restrict__ tok, int BT,
+                                                       int Vp, int nch, int nsb,
+                                                       const int* __restrict__ scan,
+                                                       const int* __restrict__ bsum,
+                                                       const int* __restrict__ rank,
+                                                       int* __restrict__ sorted) {
+    const int p = blockIdx.x * blockDim.x + threadIdx.x;
+    if (p >= BT) return;
+    const int v = tok[p];
+    if (v < 0 || v >= Vp) return;
+    const int64_t idx = (int64_t)v * nch + p / ENC_CHUNK;
+    sorted[scan[idx] + bsum[idx / ENC_SCAN] + rank[p]] = p;
 }
 
-// One block per (token, 256-channel slice). Each thread owns one channel and
-// sums the gradient rows of the token's positions in increasing position
-// order, then adds the total to dwte; the order depends only on the
-// positions, so the result is deterministic. Ordering: a bucket of at most 256
-// positions is ranked by counting (positions are distinct); a larger one marks
-// its positions in an LDS bitmap of BT bits that every thread walks upwards.
-#define ENC_SMALL 256
+// Sorted slot range [begin, end) of token v's positions.
+struct EncSeg {
+    const int* scan;
+    const int* bsum;
+    int nch, Vp;
+    __device__ __forceinline__ int begin(int v) const {
+        const int64_t idx = (int64_t)v * nch;
+        return scan[idx] + bsum[idx / ENC_SCAN];
+    }
+    __device__ __forceinline__ int end(int v) const {
+        if (v + 1 < Vp) return begin(v + 1);
+        const int64_t n = (int64_t)Vp * nch;  // the sorted count is the scan total
+        return bsum[(n + ENC_SCAN - 1) / ENC_SCAN];
+    }
+};
+
+// Adds dout rows sorted[i0..i1) (8 channels from c8 * 8) to s, in slot order.
 template <typename T>
-__global__ __launch_bounds__(256) void encoder_bwd_wte_kernel(float* __restrict__ dwte,
-                                                              const T* __restrict__ dout,
-                                                              const int* __restrict__ offset,
-                                                              const int* __restrict__ bucket,
-                                                              int C, int BT) {
-    extern __shared__ unsigned int enc_lds[];
-    const int v = blockIdx.x, tid = threadIdx.x;
-    const int b0 = offset[v], n = offset[v + 1] - b0;
-    if (n == 0) return;
-    const int c = blockIdx.y * blockDim.x + tid;
-    float s = 0.f;
-    if (n <= ENC_SMALL) {
-        int* raw = reinterpret_cast<int*>(enc_lds);
-        int* pos = raw + ENC_SMALL;
-        int mine = tid < n ? bucket[b0 + tid] : 0;
-        if (tid < n) raw[tid] = mine;
-        __syncthreads();
-        if (tid < n) {
-            int rank = 0;
-            for (int j = 0; j < n; j++) rank += raw[j] < mine;
-            pos[rank] = mine;
-        }
-        __syncthreads();
-        if (c < C)
-            for (int i = 0; i < n; i++) s += to_f32(dout[(int64_t)pos[i] * C + c]);
-    } else {
-        const int nw = (BT + 31) / 32;
-        for (int i = tid; i < nw; i += blockDim.x) enc_lds[i] = 0u;
-        __syncthreads();
-        for (int i = tid; i < n; i += blockDim.x) {
-            int p = bucket[b0 + i];
-            atomicOr(&enc_lds[p >> 5], 1u << (p & 31));
-        }
-        __syncthreads();
-        if (c < C)
-            for (int w = 0; w < nw; w++) {
-                unsigned int bits = enc_lds[w];
-                while (bits) {
-                    int p = w * 32 + __builtin_ctz(bits);
-                    bits &= bits - 1;
-                    s += to_f32(dout[(int64_t)p * C + c]);
-                }
-            }
+__device__ __forceinline__ void enc_sum_rows(float (&s)[8], const T* __restrict__ dout,
+                                             const int* __restrict__ sorted, int i0, int i1,
+                                             int C, int c8) {
+    int i = i0;
+    for (; i + 4 <= i1; i += 4) {
+        float r[4][8];
+#pragma unroll
+        for (int u = 0; u < 4; u++) load8(dout + (int64_t)sorted[i + u] * C + c8 * 8, r[u]);
+#pragma unroll
+        for (int u = 0; u < 4; u++)
+#pragma unroll
+            for (int k = 0; k < 8; k++) s[k] += r[u][k];
     }
-    if (c < C) dwte[(int64_t)v * C + c] += s;
+    for (; i < i1; i++) {
+        float r[8];
+        load8(dout + (int64_t)sorted[i] * C + c8 * 8, r);
+#pragma unroll
+        for (int k = 0; k < 8; k++) s[k] += r[k];
+    }
+}
+
+__device__ __forceinline__ void enc_add_row(float* __restrict__ dst, const float (&s)[8]) {
+    floatx4* d = reinterpret_cast<floatx4*>(dst);
+    floatx4 a = d[0], b = d[1];
+    a += floatx4{s[0], s[1], s[2], s[3]};
+    b += floatx4{s[4], s[5], s[6], s[7]};
+    d[0] = a;
+    d[1] = b;
+}
+
+// One block per range of ENC_RANGE sorted slots; thread t owns channels
+// 8t.. (looping when C/8 > blockDim).
+template <typename T>
+__global__ __launch_bounds__(128) void enc_range_kernel(float* __restrict__ dwte,
+                                                        float* __restrict__ piece,
+                                                        const T* __restrict__ dout,
+                                                        const int32_t* __restrict__ tok,
+                                                        const int* __restrict__ sorted,
+                                                        EncSeg seg, int C) {
+    const int b = blockIdx.x;
+    const int total = seg.end(seg.Vp - 1);
+    const int lo = b * ENC_RANGE, hi = min(total, lo + ENC_RANGE);
+    if (lo >= hi) return;
+    for (int c8 = threadIdx.x; c8 < C / 8; c8 += blockDim.x) {
+        int i = lo;
+        while (i < hi) {
+            const int v = tok[sorted[i]];
+            const int sb = seg.begin(v), se = seg.end(v);
+            const int e = max(i + 1, min(hi, se));  // always advances
+            float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            enc_sum_rows(s, dout, sorted, i, e, C, c8);
+            float* dst;
+            if (sb >= lo && se <= hi) dst = dwte + (int64_t)v * C;        // whole segment
+            else dst = piece + ((int64_t)b * 2 + (sb < lo ? 0 : 1)) * C;  // head / tail piece
+            if (sb >= lo && se <= hi) enc_add_row(dst + c8 * 8, s);
+            else {
+                floatx4* d = reinterpret_cast<floatx4*>(dst + c8 * 8);
+                d[0] = floatx4{s[0], s[1], s[2], s[3]};
+                d[1] = floatx4{s[4], s[5], s[6], s[7]};
+            }
+            i = e;
+        }
+    }
+}
+
+// One block per range boundary b*ENC_RANGE: the token whose segment crosses
+// it for the first time is finished here, its pieces added in range order.
+__global__ __launch_bounds__(128) void enc_fix_kernel(float* __restrict__ dwte,
+                                                      const float* __restrict__ piece,
+                                                      const int32_t* __restrict__ tok,
+                                                      const int* __restrict__ sorted, EncSeg seg,
+                                                      int C) {
+    const int b = blockIdx.x + 1;
+    const int total = seg.end(seg.Vp - 1);
+    const int cut = b * ENC_RANGE;
+    if (cut >= total) return;
+    const int v = tok[sorted[cut - 1]];
+    if (tok[sorted[cut]] != v) return;
+    const int sb = seg.begin(v), se = seg.end(v);
+    if (sb < cut - ENC_RANGE) return;  // crossed an earlier boundary first
+    const int bs = b - 1, be = (se - 1) / ENC_RANGE;
+    for (int c8 = threadIdx.x; c8 < C / 8; c8 += blockDim.x) {
+        float s[8];
+        const float* t = piece + ((int64_t)bs * 2 + 1) * C + c8 * 8;
+#pragma unroll
+        for (int k = 0; k < 8; k++) s[k] = t[k];
+        for (int r = bs + 1; r <= be; r++) {
+            const float* h = piece + ((int64_t)r * 2) * C + c8 * 8;
+#pragma unroll
+            for (int k = 0; k < 8; k++) s[k] += h[k];
+        }
+        enc_add_row(dwte + (int64_t)v * C + c8 * 8, s);
+    }
 }
 
 template <typename T>
 void encoder_bwd(float* dwte, float* dwpe, const T* dout, const int32_t* tok, int B, int Tn,
-                 int C, int Vp, int maxT, int* ws_count, int* ws_cursor, int* ws_offset,
-                 int* ws_bucket, hipStream_t st) {
-    const int n = B * Tn;
+                 int C, int Vp, int maxT, void* ws, hipStream_t st) {
+    const int BT = B * Tn;
     encoder_bwd_wpe_kernel<T><<<ceil_div((int64_t)maxT * C, 256), 256, 0, st>>>(dwpe, dout, B, Tn,
                                                                                 C, maxT);
-    fill_zero_i32(ws_count, Vp, st);
-    token_count_kernel<<<ceil_div(n, 256), 256, 0, st>>>(tok, n, Vp, ws_count);
-    token_scan_kernel<<<1, 1024, 0, st>>>(ws_count, Vp, ws_offset, ws_cursor);
-    token_fill_kernel<<<ceil_div(n, 256), 256, 0, st>>>(tok, n, Vp, ws_offset, ws_cursor,
-                                                        ws_bucket);
-    dim3 grid(Vp, ceil_div(C, 256));
-    size_t lds = (size_t)((n + 31) / 32) * 4;
-    if (lds < 2 * ENC_SMALL * sizeof(int)) lds = 2 * ENC_SMALL * sizeof(int);
-    encoder_bwd_wte_kernel<T><<<grid, 256, lds, st>>>(dwte, dout, ws_offset, ws_bucket, C, n);
+    const EncWs w = enc_ws(ws, BT, Vp, C);
+    const int64_t ncount = (int64_t)Vp * w.nch;
+    fill_zero_i32(w.scan, ncount, st);
+    enc_rank_kernel<<<w.nch, 1024, 0, st>>>(tok, BT, Vp, w.nch, w.scan, w.rank);
+    enc_scan_block_kernel<<<w.nsb, 1024, 0, st>>>(w.scan, ncount, w.bsum);
+    enc_scan_totals_kernel<<<1, 1024, 0, st>>>(w.bsum, w.nsb);
+    enc_fill_kernel<<<ceil_div(BT, 256), 256, 0, st>>>(tok, BT, Vp, w.nch, w.nsb, w.scan, w.bsum,
+                                                       w.rank, w.sorted);
+    const EncSeg seg{w.scan, w.bsum, w.nch, Vp};
+    enc_range_kernel<T><<<w.nr, 128, 0, st>>>(dwte, w.piece, dout, tok, w.sorted, seg, C);
+    if (w.nr > 1)
+        enc_fix_kernel<<<w.nr - 1, 128, 0, st>>>(dwte, w.piece, tok, w.sorted, seg, C);
 }
 
 template void encoder_fwd<float>(float*, const int32_t*, const float*, const float*, int, int,
@@ -181,6 +354,6 @@ template void encoder_fwd<float>(float*, const int32_t*, const float*, const flo
 template void encoder_fwd<bf16>(bf16*, const int32_t*, const bf16*, const bf16*, int, int, int,
                                 int, int*, hipStream_t);
 template void encoder_bwd<float>(float*, float*, const float*, const int32_t*, int, int, int, int,
-                                 int, int*, int*, int*, int*, hipStream_t);
+                                 int, void*, hipStream_t);
 template void encoder_bwd<bf16>(float*, float*, const bf16*, const int32_t*, int, int, int, int,
-                                int, int*, int*, int*, int*, hipStream_t);
+                                int, void*, hipStream_t);

@@ -42,8 +42,8 @@ enum {
     A_ENCODED, A_LN1, A_LN1_MEAN, A_LN1_RSTD, A_QKV, A_ATTY, A_ATT_LSE, A_RESIDUAL2,
     A_LN2, A_LN2_MEAN, A_LN2_RSTD, A_FCH, A_FCH_GELU, A_RESIDUAL3, A_LNF, A_LNF_MEAN,
     A_LNF_RSTD, A_LOGITS, A_LOSSES, A_LOSS, A_ERR,
-    W_DRES, W_DC, W_D3C, W_D4C, W_ATT_D, W_LN_PART, W_BIAS_PART, W_ENC_COUNT, W_ENC_CURSOR,
-    W_ENC_OFFSET, W_ENC_BUCKET, W_DW_SPLIT, NUM_A
+    W_DRES, W_DC, W_D3C, W_D4C, W_ATT_D, W_LN_PART, W_BIAS_PART, W_ENC,
+    W_DW_SPLIT, NUM_A
 };
 
 const char* const A_NAMES[NUM_A] = {
@@ -51,7 +51,7 @@ const char* const A_NAMES[NUM_A] = {
     "ln2", "ln2_mean", "ln2_rstd", "fch", "fch_gelu", "residual3", "lnf", "lnf_mean",
     "lnf_rstd", "logits", "losses", "loss", "err",
     "dresidual", "dbuf_c", "dbuf_3c", "dbuf_4c", "att_d", "ln_partials", "bias_partials",
-    "enc_count", "enc_cursor", "enc_offset", "enc_bucket", "dw_split"};
+    "enc_work", "dw_split"};
 
 constexpr int64_t ALIGN = 256;
 int64_t align_up(int64_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
@@ -139,9 +139,7 @@ void plan(const gpt2_config* c, Layout* lay) {
     a[W_ATT_D] = 2 * B * NH * T * 4;  // D, then the base-2 log-sum-exp
     a[W_LN_PART] = layernorm_bwd_partials((int)C) * 4;
     a[W_BIAS_PART] = bias_bwd_partials((int)BT, (int)(4 * C)) * 4;
-    a[W_ENC_COUNT] = a[W_ENC_CURSOR] = V * 4;
-    a[W_ENC_OFFSET] = (V + 1) * 4;
-    a[W_ENC_BUCKET] = BT * 4;
+    a[W_ENC] = encoder_bwd_workspace_bytes((int)BT, (int)V, (int)C);
     // split-reduction partials of the bf16 weight-gradient products
     int64_t dwf = 0;
     if (c->dtype == GPT2_DTYPE_BF16) {
@@ -456,8 +454,7 @@ void backward_impl(gpt2* h) {
     {
         KScope k(h, K_ENCODER_BWD, nC * es + 4.0 * c.max_T * C + 8.0 * BT);
         encoder_bwd<T>(G[P_WTE], G[P_WPE], dres, h->last_inputs, B, Tn, C, Vp, c.max_T,
-                       (int*)h->a[W_ENC_COUNT], (int*)h->a[W_ENC_CURSOR],
-                       (int*)h->a[W_ENC_OFFSET], (int*)h->a[W_ENC_BUCKET], st);
+                       h->a[W_ENC], st);
     }
 }
 

@@ -11,13 +11,14 @@
 template <typename T>
 void encoder_fwd(T* out, const int32_t* tok, const T* wte, const T* wpe, int B, int Tn, int C,
                  int V, int* err, hipStream_t st);
-// dwte[tok[b,t],:] += dout[b,t,:] (deterministic: positions of one token are
-// summed in increasing order); dwpe[t,:] = sum_b dout[b,t,:], rows >= Tn = 0.
-// ws_*: int32 workspaces of Vp, Vp, Vp+1 and B*Tn elements.
+// dwte[tok[b,t],:] += dout[b,t,:] (deterministic: the positions of one token
+// are summed in increasing order, in a fixed grouping); dwpe[t,:] =
+// sum_b dout[b,t,:], rows >= Tn = 0. ws: encoder_bwd_workspace_bytes(B*Tn,
+// Vp, C) bytes, 256-byte aligned. C % 8 == 0.
+int64_t encoder_bwd_workspace_bytes(int BT, int Vp, int C);
 template <typename T>
 void encoder_bwd(float* dwte, float* dwpe, const T* dout, const int32_t* tok, int B, int Tn,
-                 int C, int Vp, int maxT, int* ws_count, int* ws_cursor, int* ws_offset,
-                 int* ws_bucket, hipStream_t st);
+                 int C, int Vp, int maxT, void* ws, hipStream_t st);
 
 // ---- LayerNorm --------------------------------------------------------------
 template <typename T>

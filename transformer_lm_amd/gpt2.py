@@ -122,7 +122,7 @@ def act_buffer_bytes(cfg):
 
 _F32_ACTS = {"ln1_mean", "ln1_rstd", "ln2_mean", "ln2_rstd", "lnf_mean", "lnf_rstd", "att_lse",
              "losses", "loss", "att_d", "ln_partials", "bias_partials"}
-_I32_ACTS = {"err", "enc_count", "enc_cursor", "enc_offset", "enc_bucket"}
+_I32_ACTS = {"err", "enc_work"}
 
 
 class GPT2:
