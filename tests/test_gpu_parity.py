@@ -92,6 +92,23 @@ def test_fp32_step_matches_oracle(name):
     assert dth[~small].max() <= 1e-4 * w.lr + 1e-6 * np.abs(ref["params"]).max()
 
 
+def test_fp32_step_skewed_tokens():
+    """Tokens drawn almost all from a few ids: one token's positions span many
+    of the summation ranges of the embedding backward (and two position
+    chunks), so its pieces go through the in-order fix-up."""
+    w = replace(WORKLOADS["tiny"], name="tiny_skewed", B=40, T=32, token_dist="zipf", zipf_s=4.0,
+                steps=1)
+    p, toks = _inputs(w)
+    x, _ = synth.split_batch(toks[0])
+    counts = np.bincount(x.ravel(), minlength=w.V)
+    say(f"fp32 step tiny_skewed: B*T={w.B * w.T}, largest bucket {counts.max()}")
+    assert counts.max() > 20 * 32  # spans more than 20 ranges of 32 positions
+    gpu = gpu_steps(w, p, toks, 1)
+    ref = oracle_steps(w, p, toks, 1)
+    rep = check_fp32(w, gpu, ref)
+    say({k: f"{v:.2e}" for k, v in rep.items()})
+
+
 @pytest.mark.parametrize("name", ["tiny", "gpt2_124m_fp32"])
 def test_fp32_intermediates_match_oracle(name):
     """Forward activations in dependency order: the first to fail is the bug."""
