@@ -14,34 +14,56 @@ __device__ __forceinline__ void adamw_one(float& th, float g, float& m, float& v
     th -= lr * (mhat / (sqrtf(vhat) + eps) + wd * th);
 }
 
+// Each thread handles two float4 groups per iteration (8 loads in flight);
+// the streams are touched once, so loads and stores bypass cache retention.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4 ld_nt(const float* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+}
+__device__ __forceinline__ void st_nt(float* p, f32x4 x) {
+    __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(p));
+}
+
 __global__ __launch_bounds__(256) void adamw_kernel(float* __restrict__ theta,
                                                     const float* __restrict__ g,
                                                     float* __restrict__ m, float* __restrict__ v,
                                                     bf16* __restrict__ theta_bf16, int64_t n,
                                                     float lr, float b1, float b2, float eps,
                                                     float wd, float c1, float c2) {
-    const int64_t n4 = n / 4;
+    typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    const int64_t n8 = n / 8;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n4; i += stride) {
-        float4 th = reinterpret_cast<float4*>(theta)[i];
-        const float4 gg = reinterpret_cast<const float4*>(g)[i];
-        float4 mm = reinterpret_cast<float4*>(m)[i];
-        float4 vv = reinterpret_cast<float4*>(v)[i];
-        adamw_one(th.x, gg.x, mm.x, vv.x, lr, b1, b2, eps, wd, c1, c2);
-        adamw_one(th.y, gg.y, mm.y, vv.y, lr, b1, b2, eps, wd, c1, c2);
-        adamw_one(th.z, gg.z, mm.z, vv.z, lr, b1, b2, eps, wd, c1, c2);
-        adamw_one(th.w, gg.w, mm.w, vv.w, lr, b1, b2, eps, wd, c1, c2);
-        reinterpret_cast<float4*>(theta)[i] = th;
-        reinterpret_cast<float4*>(m)[i] = mm;
-        reinterpret_cast<float4*>(v)[i] = vv;
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n8; i += stride) {
+        const int64_t e0 = i * 4, e1 = (i + n8) * 4;  // two groups n/2 apart: both streams coalesce
+        f32x4 th[2] = {ld_nt(theta + e0), ld_nt(theta + e1)};
+        const f32x4 gg[2] = {ld_nt(g + e0), ld_nt(g + e1)};
+        f32x4 mm[2] = {ld_nt(m + e0), ld_nt(m + e1)};
+        f32x4 vv[2] = {ld_nt(v + e0), ld_nt(v + e1)};
+#pragma unroll
+        for (int u = 0; u < 2; u++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                float t = th[u][e], a = mm[u][e], b = vv[u][e];
+                adamw_one(t, gg[u][e], a, b, lr, b1, b2, eps, wd, c1, c2);
+                th[u][e] = t;
+                mm[u][e] = a;
+                vv[u][e] = b;
+            }
+        st_nt(theta + e0, th[0]);
+        st_nt(theta + e1, th[1]);
+        st_nt(m + e0, mm[0]);
+        st_nt(m + e1, mm[1]);
+        st_nt(v + e0, vv[0]);
+        st_nt(v + e1, vv[1]);
         if (theta_bf16) {
-            typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
-            bf16x4 o = {(bf16)th.x, (bf16)th.y, (bf16)th.z, (bf16)th.w};
-            reinterpret_cast<bf16x4*>(theta_bf16)[i] = o;
+            *reinterpret_cast<bf16x4*>(theta_bf16 + e0) =
+                bf16x4{(bf16)th[0][0], (bf16)th[0][1], (bf16)th[0][2], (bf16)th[0][3]};
+            *reinterpret_cast<bf16x4*>(theta_bf16 + e1) =
+                bf16x4{(bf16)th[1][0], (bf16)th[1][1], (bf16)th[1][2], (bf16)th[1][3]};
         }
     }
-    // tail (n % 4 elements)
-    for (int64_t i = n4 * 4 + blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += stride) {
+    // tail (n % 8 elements)
+    for (int64_t i = n8 * 8 + blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += stride) {
         float th = theta[i], mm = m[i], vv = v[i];
         adamw_one(th, g[i], mm, vv, lr, b1, b2, eps, wd, c1, c2);
         theta[i] = th;
@@ -54,7 +76,7 @@ __global__ __launch_bounds__(256) void adamw_kernel(float* __restrict__ theta,
 void adamw(float* theta, const float* g, float* m, float* v, bf16* theta_bf16, int64_t n,
            float lr, float b1, float b2, float eps, float wd, float c1, float c2,
            hipStream_t st) {
-    int64_t blocks = (n / 4 + 255) / 256;
+    int64_t blocks = (n / 8 + 255) / 256;
     if (blocks > 8192) blocks = 8192;
     if (blocks < 1) blocks = 1;
     adamw_kernel<<<(int)blocks, 256, 0, st>>>(theta, g, m, v, theta_bf16, n, lr, b1, b2, eps, wd,

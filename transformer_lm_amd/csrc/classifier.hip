@@ -9,7 +9,8 @@
 
 // One block per row: pass 1 keeps a per-thread running (max, sum of exp)
 // over 8-column chunks, merged across the block; pass 2 writes
-// dz = (exp(z - lse) - [v == target]) * dloss.
+// dz = (exp(z - lse) - [v == target]) * dloss. Used for vocabularies too wide
+// for the register-resident kernel below (more than 13 * 4096 columns).
 template <typename T>
 __global__ __launch_bounds__(CL_THREADS) void classifier_kernel(T* logits,
                                                                 float* __restrict__ losses,
@@ -61,10 +62,106 @@ __global__ __launch_bounds__(CL_THREADS) void classifier_kernel(T* logits,
     }
 }
 
+// Single HBM pass: each thread keeps its NCHK chunks of 8 logits in registers
+// (the row is read once), runs the online (max, sum of exp) over them, and
+// after the block-wide merge writes the gradients from the same registers.
+// exp(x) is evaluated as 2^(x log2 e) on the hardware exponential.
+#define CL_LOG2E 1.4426950408889634f
+
+// Storage-typed chunk of 8 logits (bf16 rows stay packed in registers).
+template <typename T>
+struct Chunk8 {
+    T x[8];
+    __device__ __forceinline__ float operator[](int i) const { return to_f32(x[i]); }
+    // Makes the chunk opaque to the compiler, so values converted to fp32 in
+    // the first pass are not kept alive until the second (which would double
+    // the registers of a bf16 row and halve the blocks per CU).
+    __device__ __forceinline__ void launder() {
+        typedef unsigned int u32v __attribute__((ext_vector_type(sizeof(T) * 2)));
+        u32v r = *reinterpret_cast<u32v*>(x);
+        asm volatile("" : "+v"(r));
+        *reinterpret_cast<u32v*>(x) = r;
+    }
+};
+
+template <typename T, int NCHK>
+__global__ __launch_bounds__(CL_THREADS) __attribute__((amdgpu_waves_per_eu(4))) void classifier_reg_kernel(
+    T* logits, float* __restrict__ losses, const int32_t* __restrict__ targets, int V, int Vp,
+    float dloss, int* err) {
+    __shared__ float red[16];
+    const int64_t row = blockIdx.x;
+    T* z = logits + row * Vp;
+    const int tgt = targets[row];
+    const bool ok = tgt >= 0 && tgt < V;
+    Chunk8<T> v[NCHK];
+#pragma unroll
+    for (int k = 0; k < NCHK; k++) {
+        const int c = (threadIdx.x + k * CL_THREADS) * 8;
+        if (c < Vp) v[k] = *reinterpret_cast<const Chunk8<T>*>(z + c);
+    }
+    float m = -INFINITY, s = 0.f;
+#pragma unroll
+    for (int k = 0; k < NCHK; k++) {
+        const int c = (threadIdx.x + k * CL_THREADS) * 8;
+        if (c < V) {
+            float cm = m;
+#pragma unroll
+            for (int i = 0; i < 8; i++)
+                if (c + i < V) cm = fmaxf(cm, v[k][i]);
+            const float cl = cm * CL_LOG2E;
+            float cs = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; i++)
+                if (c + i < V) cs += __builtin_amdgcn_exp2f(fmaf(v[k][i], CL_LOG2E, -cl));
+            s = s * __builtin_amdgcn_exp2f((m - cm) * CL_LOG2E) + cs;
+            m = cm;
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < NCHK; k++) v[k].launder();
+    const float M = block_max(m, red);
+    const float S = block_sum(m == -INFINITY ? 0.f : s * __builtin_amdgcn_exp2f((m - M) * CL_LOG2E), red);
+    const float lse = M + logf(S);
+    if (threadIdx.x == 0) {
+        if (ok) {
+            losses[row] = lse - to_f32(z[tgt]);
+        } else {
+            losses[row] = 0.f;
+            atomicOr(err, 1);
+        }
+    }
+    __syncthreads();  // the target logit is read before any thread overwrites it
+    const float l2 = lse * CL_LOG2E;
+#pragma unroll
+    for (int k = 0; k < NCHK; k++) {
+        const int c = (threadIdx.x + k * CL_THREADS) * 8;
+        if (c < Vp) {
+            float d[8];
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                const int col = c + i;
+                d[i] = col < V ? (__builtin_amdgcn_exp2f(fmaf(v[k][i], CL_LOG2E, -l2)) -
+                                  (col == tgt ? 1.f : 0.f)) *
+                                     dloss
+                               : 0.f;
+            }
+            store8(z + c, d);
+        }
+    }
+}
+
 template <typename T>
 void classifier_fwd(T* logits, float* losses, const int32_t* targets, int N, int V, int Vp,
                     float dloss, int* err, hipStream_t st) {
-    classifier_kernel<T><<<N, CL_THREADS, 0, st>>>(logits, losses, targets, V, Vp, dloss, err);
+    const int nchk = ceil_div(Vp, 8 * CL_THREADS);
+    if (nchk <= 1)
+        classifier_reg_kernel<T, 1><<<N, CL_THREADS, 0, st>>>(logits, losses, targets, V, Vp, dloss, err);
+    else if (nchk <= 4)
+        classifier_reg_kernel<T, 4><<<N, CL_THREADS, 0, st>>>(logits, losses, targets, V, Vp, dloss, err);
+    else if (nchk <= 13)
+        classifier_reg_kernel<T, 13><<<N, CL_THREADS, 0, st>>>(logits, losses, targets, V, Vp, dloss, err);
+    else
+        classifier_kernel<T><<<N, CL_THREADS, 0, st>>>(logits, losses, targets, V, Vp, dloss, err);
 }
 
 __global__ __launch_bounds__(1024) void loss_mean_kernel(float* out, const float* __restrict__ l,

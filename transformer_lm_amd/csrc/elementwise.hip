@@ -1,9 +1,7 @@
 // Elementwise kernels: tanh-GELU forward/backward, fills, fp32 -> bf16 rounding.
 // HBM-bound: 16-byte (8 x bf16) or 2 x 16-byte (8 x fp32) accesses per thread.
+#include "gelu.h"
 #include "kernels.h"
-
-#define GELU_K 0.7978845608028654f  // sqrt(2/pi)
-#define GELU_C 0.044715f
 
 // GELU in its tanh form (the MLP activation of GPT-2):
 // g(x) = x/2 (1 + tanh(a)), a = sqrt(2/pi) (x + 0.044715 x^3).

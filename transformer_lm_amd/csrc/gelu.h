@@ -1,0 +1,29 @@
+// tanh-GELU, the MLP activation of GPT-2 (page "Building GPT-2 from scratch",
+// section on the MLP block; page "llm.c: Large Language Model Training in Pure
+// C/CUDA Without Dependencies", the GELU kernel):
+//   g(x) = x/2 (1 + tanh a),  a = sqrt(2/pi) (x + 0.044715 x^3).
+// With s = 1 / (1 + exp(-2a)) = (1 + tanh a)/2 the same function is g = x s,
+// and its derivative g' = s + 2 x s (1 - s) da/dx, da/dx = sqrt(2/pi)
+// (1 + 3 * 0.044715 x^2). That form costs one exponential and one reciprocal
+// on the hardware units; it is used where GELU rides in a matrix-product
+// epilogue.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#define GELU_K 0.7978845608028654f  // sqrt(2/pi)
+#define GELU_C 0.044715f
+#define GELU_M2LOG2E (-2.8853900817779268f)  // -2 log2(e)
+
+__device__ __forceinline__ float gelu_sigmoid_2a(float x) {
+    const float a = GELU_K * fmaf(GELU_C * x, x * x, x);
+    return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(GELU_M2LOG2E * a));
+}
+
+__device__ __forceinline__ float gelu_fast(float x) { return x * gelu_sigmoid_2a(x); }
+
+__device__ __forceinline__ float gelu_grad_fast(float x) {
+    const float s = gelu_sigmoid_2a(x);
+    const float da = GELU_K * fmaf(3.f * GELU_C * x, x, 1.f);
+    return fmaf(2.f * x * s * (1.f - s), da, s);
+}

@@ -27,6 +27,7 @@
 // addresses and their outputs discarded.
 #pragma once
 
+#include "gelu.h"
 #include "gemm_mfma.h"
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -151,10 +152,10 @@ struct LdsOperand {
 // row over their reduction range (for dW = dy^T x: the bias gradient).
 template <int BM, int BN, int BK, int WM, int WN, int GM, int S, bool XRC, bool YRC, int EPI>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_lds_kernel(
-    void* __restrict__ out_, const bf16* __restrict__ X, const bf16* __restrict__ Y,
-    const bf16* __restrict__ bias, const bf16* __restrict__ residual, int M, int N, int K,
-    int ldx, int ldy, int ldo, int kchunk, int64_t split_stride, float* __restrict__ rowsum,
-    int64_t rowsum_stride) {
+    void* __restrict__ out_, bf16* __restrict__ out2, const bf16* __restrict__ X,
+    const bf16* __restrict__ Y, const bf16* __restrict__ bias, const bf16* __restrict__ residual,
+    int M, int N, int K, int ldx, int ldy, int ldo, int kchunk, int64_t split_stride,
+    float* __restrict__ rowsum, int64_t rowsum_stride) {
     constexpr int NW = WM * WN, NT = NW * 64;
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int FM = TM / 32, FN = TN / 32;
@@ -296,17 +297,29 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_lds_kernel(
 #pragma unroll
                         for (int e = 0; e < 8; e++) v[e] += (float)bv[e];
                     }
-                    if (residual) {
+                    if (EPI == EPI_BF16 && residual) {
                         const bf16x8 rv =
                             *reinterpret_cast<const bf16x8*>(residual + (int64_t)i * ldo + j);
 #pragma unroll
                         for (int e = 0; e < 8; e++) v[e] += (float)rv[e];
+                    }
+                    if (EPI == EPI_BF16_DGELU) {
+                        const bf16x8 xv =
+                            *reinterpret_cast<const bf16x8*>(residual + (int64_t)i * ldo + j);
+#pragma unroll
+                        for (int e = 0; e < 8; e++) v[e] *= gelu_grad_fast((float)xv[e]);
                     }
                     bf16x8 o;
 #pragma unroll
                     for (int e = 0; e < 8; e++) o[e] = (bf16)v[e];
                     *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(out_) + (int64_t)i * ldo +
                                                j) = o;
+                    if (EPI == EPI_BF16_GELU) {
+                        bf16x8 ga;
+#pragma unroll
+                        for (int e = 0; e < 8; e++) ga[e] = (bf16)gelu_fast((float)o[e]);
+                        *reinterpret_cast<bf16x8*>(out2 + (int64_t)i * ldo + j) = ga;
+                    }
                 }
             }
         }
@@ -322,12 +335,12 @@ struct GemmLds {
     static void run(void* out, const bf16* X, const bf16* Y, const bf16* bias,
                     const bf16* residual, int M, int N, int K, int ldx, int ldy, int ldo,
                     int splits, int kchunk, int64_t split_stride, float* rowsum,
-                    int64_t rowsum_stride, hipStream_t st) {
+                    int64_t rowsum_stride, hipStream_t st, bf16* out2 = nullptr) {
         const int tiles = ceil_div(M, BM) * ceil_div(N, BN);
         dim3 grid(tiles, 1, splits);
         gemm_lds_kernel<BM, BN, BK, WM, WN, GM, S, XRC, YRC, EPI>
-            <<<grid, WM * WN * 64, lds_bytes, st>>>(out, X, Y, bias, residual, M, N, K, ldx, ldy,
-                                                    ldo, kchunk, split_stride, rowsum,
+            <<<grid, WM * WN * 64, lds_bytes, st>>>(out, out2, X, Y, bias, residual, M, N, K, ldx,
+                                                    ldy, ldo, kchunk, split_stride, rowsum,
                                                     rowsum_stride);
     }
 

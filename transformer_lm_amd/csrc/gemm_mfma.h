@@ -94,7 +94,10 @@ struct Stager {
 };
 
 // EPI_BF16: out bf16 = acc (+ bias) (+ residual);  EPI_F32: out fp32 = acc.
-enum { EPI_BF16 = 0, EPI_F32 = 1 };
+// Direct-to-LDS kernel only: EPI_BF16_GELU: out = bf16(acc + bias), out2 =
+// bf16(gelu(out)); EPI_BF16_DGELU: out = bf16(acc * gelu'(aux)) with aux the
+// bf16 pre-activation (passed as `residual`).
+enum { EPI_BF16 = 0, EPI_F32 = 1, EPI_BF16_GELU = 2, EPI_BF16_DGELU = 3 };
 
 // Tile coordinates of block `bid` of `total` = nbm x nbn tiles (see the file
 // comment): XCD-contiguous ranges, GM-row groups walked column by column.

@@ -37,7 +37,9 @@ static void prepare_lds_kernels() {
     static std::once_flag once;
     std::call_once(once, [] {
         (void)FwdCfg::prepare<false, false, EPI_BF16>();
+        (void)FwdCfg::prepare<false, false, EPI_BF16_GELU>();
         (void)FwdCfg::prepare<false, true, EPI_BF16>();
+        (void)FwdCfg::prepare<false, true, EPI_BF16_DGELU>();
         (void)DwCfg::prepare<true, true, EPI_F32>();
     });
 }
@@ -66,6 +68,28 @@ void gemm_bf16_bwd_dx(bf16* dinp, const bf16* dout, const bf16* w, int M, int N,
     }
     Cfg::run<false, true, EPI_BF16>(dinp, dout, w, nullptr, nullptr, M, K, N, N, K, K, 1, N, 0,
                                     nullptr, 0, st);
+}
+
+// out = inp . w^T + bias and out_gelu = gelu(out) (both bf16) in one pass;
+// false (nothing launched) when K is not a multiple of the tile depth.
+bool gemm_bf16_fwd_gelu(bf16* out, bf16* out_gelu, const bf16* inp, const bf16* w,
+                        const bf16* bias, int M, int K, int N, hipStream_t st) {
+    if (K % LDS_BK != 0) return false;
+    prepare_lds_kernels();
+    FwdCfg::run<false, false, EPI_BF16_GELU>(out, inp, w, bias, nullptr, M, N, K, K, K, N, 1, K, 0,
+                                             nullptr, 0, st, out_gelu);
+    return true;
+}
+
+// dinp = (dout . w) * gelu'(pre), pre [M, K] the bf16 pre-activation; false
+// (nothing launched) when N is not a multiple of the tile depth.
+bool gemm_bf16_bwd_dx_dgelu(bf16* dinp, const bf16* dout, const bf16* w, const bf16* pre, int M,
+                            int N, int K, hipStream_t st) {
+    if (N % LDS_BK != 0) return false;
+    prepare_lds_kernels();
+    FwdCfg::run<false, true, EPI_BF16_DGELU>(dinp, dout, w, nullptr, pre, M, K, N, N, K, K, 1, N, 0,
+                                             nullptr, 0, st);
+    return true;
 }
 
 // Splits of the B*T reduction of a weight gradient [N, K]. Cost model, in

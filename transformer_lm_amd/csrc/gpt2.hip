@@ -301,12 +301,17 @@ void forward_impl(gpt2* h, const int32_t* in, const int32_t* tg) {
             layernorm_fwd<T>(ln2_l, ln2m + (int64_t)l * BT, ln2r + (int64_t)l * BT, res2_l,
                              P[P_LN2W] + l * C, P[P_LN2B] + l * C, BT, C, st);
         }
-        {
+        if (std::is_same<T, bf16>::value) {
+            // bf16: the GELU is applied in the product's epilogue
             KScope k(h, K_MATMUL_FWD, mm_flops(BT, 4 * C, C));
-            matmul_fwd<T>(fch_l, ln2_l, P[P_FCW] + (int64_t)l * 4 * C * C, P[P_FCB] + l * 4 * C,
-                          nullptr, BT, C, 4 * C, st);
-        }
-        {
+            matmul_fwd_gelu<T>(fch_l, fchg_l, ln2_l, P[P_FCW] + (int64_t)l * 4 * C * C,
+                               P[P_FCB] + l * 4 * C, BT, C, 4 * C, st);
+        } else {
+            {
+                KScope k(h, K_MATMUL_FWD, mm_flops(BT, 4 * C, C));
+                matmul_fwd<T>(fch_l, ln2_l, P[P_FCW] + (int64_t)l * 4 * C * C,
+                              P[P_FCB] + l * 4 * C, nullptr, BT, C, 4 * C, st);
+            }
             KScope k(h, K_GELU_FWD, 2.0 * 4 * nC * es);
             gelu_fwd<T>(fchg_l, fch_l, 4 * nC, st);
         }
@@ -391,7 +396,12 @@ void backward_impl(gpt2* h) {
         const T* res = l == 0 ? encoded : res3 + (l - 1) * nC;
         const int64_t w4 = (int64_t)l * 4 * C * C;
         // MLP: dres is dLoss/d(x2), also the gradient of fcproj's output
-        {
+        if (std::is_same<T, bf16>::value) {
+            // bf16: gelu' is applied in the product's epilogue
+            KScope k(h, K_MATMUL_BWD_DX, mm_flops(BT, 4 * C, C));
+            matmul_bwd_dx_dgelu<T>(d4C, dres, P[P_FCPROJW] + w4, fch + l * 4 * nC, BT, C, 4 * C,
+                                   st);
+        } else {
             KScope k(h, K_MATMUL_BWD_DX, mm_flops(BT, 4 * C, C));
             matmul_bwd_dx<T>(d4C, dres, P[P_FCPROJW] + w4, BT, C, 4 * C, st);
         }
@@ -400,7 +410,7 @@ void backward_impl(gpt2* h) {
             matmul_bwd_dw<T>(G[P_FCPROJW] + w4, G[P_FCPROJB] + l * C, dres, fchg + l * 4 * nC, BT,
                              C, 4 * C, dws, bp, st);
         }
-        {
+        if (!std::is_same<T, bf16>::value) {
             KScope k(h, K_GELU_BWD, 3.0 * 4 * nC * es);
             gelu_bwd<T>(d4C, fch + l * 4 * nC, d4C, 4 * nC, st);
         }

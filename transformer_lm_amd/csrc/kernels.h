@@ -38,6 +38,14 @@ template <typename T>
 void matmul_fwd(T* out, const T* inp, const T* w, const T* bias, const T* residual, int M,
                 int K, int N, hipStream_t st);
 // dinp[M,K] = dout[M,N] . w[N,K]
+// out = inp . w^T + bias, out_gelu = gelu(out)
+template <typename T>
+void matmul_fwd_gelu(T* out, T* out_gelu, const T* inp, const T* w, const T* bias, int M, int K,
+                     int N, hipStream_t st);
+// dinp[M,K] = (dout[M,N] . w[N,K]) * gelu'(pre[M,K])
+template <typename T>
+void matmul_bwd_dx_dgelu(T* dinp, const T* dout, const T* w, const T* pre, int M, int N, int K,
+                         hipStream_t st);
 template <typename T>
 void matmul_bwd_dx(T* dinp, const T* dout, const T* w, int M, int N, int K, hipStream_t st);
 // dw[N,K] = dout[M,N]^T . inp[M,K] (fp32, written)
@@ -52,6 +60,10 @@ void gemm_bf16_fwd(bf16* out, const bf16* inp, const bf16* w, const bf16* bias,
                    const bf16* residual, int M, int K, int N, hipStream_t st);
 void gemm_bf16_bwd_dx(bf16* dinp, const bf16* dout, const bf16* w, int M, int N, int K,
                       hipStream_t st);
+bool gemm_bf16_fwd_gelu(bf16* out, bf16* out_gelu, const bf16* inp, const bf16* w,
+                        const bf16* bias, int M, int K, int N, hipStream_t st);
+bool gemm_bf16_bwd_dx_dgelu(bf16* dinp, const bf16* dout, const bf16* w, const bf16* pre, int M,
+                            int N, int K, hipStream_t st);
 void gemm_bf16_bwd_dw(float* dw, float* db, const bf16* dout, const bf16* inp, int M, int N,
                       int K, float* ws, hipStream_t st);
 int64_t gemm_dw_workspace_floats(int M, int N, int K);

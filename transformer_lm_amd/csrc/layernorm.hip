@@ -160,31 +160,43 @@ __global__ __launch_bounds__(256) void layernorm_bwd_kernel(
     }
 }
 
-// Sums the partial rows: a block owns 64 columns, its 16 row phases walk the
-// rows with stride 16 and are combined in phase order.
-__global__ __launch_bounds__(1024) void layernorm_bwd_reduce_kernel(
-    float* __restrict__ dw, float* __restrict__ db, const float* __restrict__ partials,
-    int nblocks, int C) {
-    __shared__ float red[16][64];
+// Sums the partial rows in two fixed-order stages. Stage 1: block (x, y) owns
+// 64 columns and partial rows [y*G, (y+1)*G) (G = nblocks / LN_RED_GROUPS); its
+// four row phases each sum every fourth row, then combine in phase order.
+// Stage 2 sums the LN_RED_GROUPS stage-1 rows of each column in order.
+#define LN_RED_GROUPS 16
+
+__global__ __launch_bounds__(256) void layernorm_bwd_reduce1_kernel(
+    float* __restrict__ stage, const float* __restrict__ partials, int nblocks, int C) {
+    __shared__ float red[4][64];
     const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
     const int j = blockIdx.x * 64 + tx;
+    const int per = (nblocks + LN_RED_GROUPS - 1) / LN_RED_GROUPS;
+    const int r0 = blockIdx.y * per, r1 = min(nblocks, r0 + per);
     float s = 0.f;
     if (j < 2 * C)
-        for (int b = ty; b < nblocks; b += 16) s += partials[(int64_t)b * 2 * C + j];
+        for (int b = r0 + ty; b < r1; b += 4) s += partials[(int64_t)b * 2 * C + j];
     red[ty][tx] = s;
     __syncthreads();
-    if (ty == 0 && j < 2 * C) {
-        float t = 0.f;
-#pragma unroll
-        for (int r = 0; r < 16; r++) t += red[r][tx];
-        if (j < C)
-            dw[j] = t;
-        else
-            db[j - C] = t;
-    }
+    if (ty == 0 && j < 2 * C)
+        stage[(int64_t)blockIdx.y * 2 * C + j] = ((red[0][tx] + red[1][tx]) + red[2][tx]) + red[3][tx];
 }
 
-int64_t layernorm_bwd_partials(int C) { return (int64_t)LN_BWD_BLOCKS * 2 * C; }
+__global__ __launch_bounds__(256) void layernorm_bwd_reduce2_kernel(
+    float* __restrict__ dw, float* __restrict__ db, const float* __restrict__ stage, int C) {
+    const int j = blockIdx.x * blockDim.x + threadIdx.x;
+    if (j >= 2 * C) return;
+    float t = 0.f;
+#pragma unroll
+    for (int r = 0; r < LN_RED_GROUPS; r++) t += stage[(int64_t)r * 2 * C + j];
+    if (j < C)
+        dw[j] = t;
+    else
+        db[j - C] = t;
+}
+
+// partial rows of the blocks, then the stage-1 rows
+int64_t layernorm_bwd_partials(int C) { return (int64_t)(LN_BWD_BLOCKS + LN_RED_GROUPS) * 2 * C; }
 
 template <typename T>
 void layernorm_bwd(T* dinp, int accumulate, float* dw, float* db, const T* dout, const T* inp,
@@ -198,7 +210,10 @@ void layernorm_bwd(T* dinp, int accumulate, float* dw, float* db, const T* dout,
     else
         layernorm_bwd_kernel<T, 4><<<nb, 256, 0, st>>>(dinp, accumulate, dout, inp, w, mean, rstd,
                                                        N, C, partials);
-    layernorm_bwd_reduce_kernel<<<ceil_div(2 * C, 64), 1024, 0, st>>>(dw, db, partials, nb, C);
+    float* stage = partials + (int64_t)LN_BWD_BLOCKS * 2 * C;
+    layernorm_bwd_reduce1_kernel<<<dim3(ceil_div(2 * C, 64), LN_RED_GROUPS), 256, 0, st>>>(
+        stage, partials, nb, C);
+    layernorm_bwd_reduce2_kernel<<<ceil_div(2 * C, 256), 256, 0, st>>>(dw, db, stage, C);
 }
 
 template void layernorm_fwd<float>(float*, float*, float*, const float*, const float*,

@@ -117,6 +117,26 @@ void matmul_bwd_dx(T* dinp, const T* dout, const T* w, int M, int N, int K, hipS
         gemm_generic<T, T, T, T>(dinp, dout, w, nullptr, nullptr, M, K, N, N, 1, 1, K, K, st);
 }
 
+// bf16: the GELU rides in the product's epilogue when the shape allows it;
+// otherwise (and for fp32) the product is followed by the elementwise kernel.
+template <typename T>
+void matmul_fwd_gelu(T* out, T* out_gelu, const T* inp, const T* w, const T* bias, int M, int K,
+                     int N, hipStream_t st) {
+    if constexpr (std::is_same<T, bf16>::value)
+        if (gemm_bf16_fwd_gelu(out, out_gelu, inp, w, bias, M, K, N, st)) return;
+    matmul_fwd<T>(out, inp, w, bias, nullptr, M, K, N, st);
+    gelu_fwd<T>(out_gelu, out, (int64_t)M * N, st);
+}
+
+template <typename T>
+void matmul_bwd_dx_dgelu(T* dinp, const T* dout, const T* w, const T* pre, int M, int N, int K,
+                         hipStream_t st) {
+    if constexpr (std::is_same<T, bf16>::value)
+        if (gemm_bf16_bwd_dx_dgelu(dinp, dout, w, pre, M, N, K, st)) return;
+    matmul_bwd_dx<T>(dinp, dout, w, M, N, K, st);
+    gelu_bwd<T>(dinp, pre, dinp, (int64_t)M * K, st);
+}
+
 template <typename T>
 void matmul_bwd_dw(float* dw, float* db, const T* dout, const T* inp, int M, int N, int K,
                    float* ws, float* bias_partials, hipStream_t st) {
@@ -188,6 +208,10 @@ void bias_bwd(float* db, const T* dout, int M, int N, float* partials, hipStream
     template void matmul_fwd<T>(T*, const T*, const T*, const T*, const T*, int, int, int,      \
                                 hipStream_t);                                                  \
     template void matmul_bwd_dx<T>(T*, const T*, const T*, int, int, int, hipStream_t);         \
+    template void matmul_fwd_gelu<T>(T*, T*, const T*, const T*, const T*, int, int, int,       \
+                                     hipStream_t);                                             \
+    template void matmul_bwd_dx_dgelu<T>(T*, const T*, const T*, const T*, int, int, int,       \
+                                         hipStream_t);                                         \
     template void matmul_bwd_dw<T>(float*, float*, const T*, const T*, int, int, int, float*,  \
                                    float*, hipStream_t);                                       \
     template void bias_bwd<T>(float*, const T*, int, int, float*, hipStream_t);
