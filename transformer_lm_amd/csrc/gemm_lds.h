@@ -150,12 +150,13 @@ struct LdsOperand {
 
 // With rowsum != nullptr, the blocks of the first column tile also sum each X
 // row over their reduction range (for dW = dy^T x: the bias gradient).
+// One output tile (tm, tn) over reduction split z (rows z*kchunk ..).
 template <int BM, int BN, int BK, int WM, int WN, int GM, int S, bool XRC, bool YRC, int EPI>
-__global__ __launch_bounds__(WM* WN * 64) void gemm_lds_kernel(
+__device__ __forceinline__ void gemm_lds_tile(
     void* __restrict__ out_, bf16* __restrict__ out2, const bf16* __restrict__ X,
     const bf16* __restrict__ Y, const bf16* __restrict__ bias, const bf16* __restrict__ residual,
     int M, int N, int K, int ldx, int ldy, int ldo, int kchunk, int64_t split_stride,
-    float* __restrict__ rowsum, int64_t rowsum_stride) {
+    float* __restrict__ rowsum, int64_t rowsum_stride, int tm, int tn, int z) {
     constexpr int NW = WM * WN, NT = NW * 64;
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int FM = TM / 32, FN = TN / 32;
@@ -169,10 +170,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_lds_kernel(
 
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int wm = wid % WM, wn = wid / WM;
-    int tm, tn;
-    tile_of<GM>(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
     const int i0 = tm * BM, j0 = tn * BN;
-    const int kbeg = blockIdx.z * kchunk;
+    const int kbeg = z * kchunk;
     const int nk = (min(K, kbeg + kchunk) - kbeg) / BK;
 
     floatx16 acc[FN][FM];
@@ -240,7 +239,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_lds_kernel(
             __builtin_amdgcn_sched_barrier(0);
         }
     }
-    if (do_rowsum && i0 + tid < M) rowsum[blockIdx.z * rowsum_stride + i0 + tid] = rsum;
+    if (do_rowsum && i0 + tid < M) rowsum[z * rowsum_stride + i0 + tid] = rsum;
     (void)NT;
     // Pin the accumulators to AGPRs: otherwise the bf16 epilogue's conversions
     // pull them into VGPRs for the whole kernel, and wide wave tiles spill.
@@ -280,7 +279,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_lds_kernel(
                 const int i = ib + r, j = jb + c;
                 if (i < M && j < N)
                     *reinterpret_cast<floatx4*>(reinterpret_cast<float*>(out_) +
-                                                blockIdx.z * split_stride + (int64_t)i * ldo + j) =
+                                                z * split_stride + (int64_t)i * ldo + j) =
                         *reinterpret_cast<const floatx4*>(stage + r * SP + c);
             }
         } else {
@@ -326,6 +325,58 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_lds_kernel(
     }
 }
 
+template <int BM, int BN, int BK, int WM, int WN, int GM, int S, bool XRC, bool YRC, int EPI>
+__global__ __launch_bounds__(WM* WN * 64) void gemm_lds_kernel(
+    void* __restrict__ out_, bf16* __restrict__ out2, const bf16* __restrict__ X,
+    const bf16* __restrict__ Y, const bf16* __restrict__ bias, const bf16* __restrict__ residual,
+    int M, int N, int K, int ldx, int ldy, int ldo, int kchunk, int64_t split_stride,
+    float* __restrict__ rowsum, int64_t rowsum_stride) {
+    int tm, tn;
+    tile_of<GM>(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
+    gemm_lds_tile<BM, BN, BK, WM, WN, GM, S, XRC, YRC, EPI>(
+        out_, out2, X, Y, bias, residual, M, N, K, ldx, ldy, ldo, kchunk, split_stride, rowsum,
+        rowsum_stride, tm, tn, blockIdx.z);
+}
+
+// A batch of independent weight-gradient products dw_p[N_p, K_p] (fp32) =
+// dout_p[R, N_p]^T . inp_p[R, K_p] over the same R rows, with db_p[N_p] = the
+// column sums of dout_p when db_p != nullptr, in one launch: the tiles of all
+// problems form one grid (no reduction splits), handed to the XCDs in
+// contiguous ranges.
+#define GROUP_MAX 64
+struct DwProblem {
+    const bf16* dout;
+    const bf16* inp;
+    float* dw;
+    float* db;
+    int N, K;
+};
+struct DwGroup {
+    int count, R;
+    int first_tile[GROUP_MAX + 1];  // prefix sums of the problems' tile counts
+    DwProblem p[GROUP_MAX];
+};
+
+template <int BM, int BN, int BK, int WM, int WN, int GM, int S>
+__global__ __launch_bounds__(WM* WN * 64) void gemm_lds_dw_group_kernel(const DwGroup g) {
+    const int total = g.first_tile[g.count];
+    const int per = total / NUM_XCD;
+    int t = blockIdx.x;
+    if (t < per * NUM_XCD) t = (t % NUM_XCD) * per + t / NUM_XCD;
+    int q = 0;
+    while (q + 1 < g.count && g.first_tile[q + 1] <= t) q++;
+    const DwProblem& pr = g.p[q];
+    const int nbm = (pr.N + BM - 1) / BM, nbn = (pr.K + BN - 1) / BN;
+    const int lt = t - g.first_tile[q];
+    // GM-row groups walked column by column, as in tile_of
+    const int gsz = GM * nbn, grp = lt / gsz, first = grp * GM;
+    const int rows = min(GM, nbm - first), r = lt - grp * gsz;
+    const int tm = first + r % rows, tn = r / rows;
+    gemm_lds_tile<BM, BN, BK, WM, WN, GM, S, true, true, EPI_F32>(
+        pr.dw, nullptr, pr.dout, pr.inp, nullptr, nullptr, pr.N, pr.K, g.R, pr.N, pr.K, pr.K,
+        g.R, 0, pr.db, 0, tm, tn, 0);
+}
+
 template <int BM, int BN, int BK, int WM, int WN, int GM, int S>
 struct GemmLds {
     static constexpr int bm = BM, bn = BN, bk = BK;
@@ -342,6 +393,16 @@ struct GemmLds {
             <<<grid, WM * WN * 64, lds_bytes, st>>>(out, out2, X, Y, bias, residual, M, N, K, ldx,
                                                     ldy, ldo, kchunk, split_stride, rowsum,
                                                     rowsum_stride);
+    }
+
+    static void run_dw_group(const DwGroup& g, hipStream_t st) {
+        gemm_lds_dw_group_kernel<BM, BN, BK, WM, WN, GM, S>
+            <<<g.first_tile[g.count], WM * WN * 64, lds_bytes, st>>>(g);
+    }
+
+    static hipError_t prepare_dw_group() {
+        return hipFuncSetAttribute((const void*)gemm_lds_dw_group_kernel<BM, BN, BK, WM, WN, GM, S>,
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
     }
 
     // Raises the kernel's dynamic-LDS limit (needed above 64 KB); call once.

@@ -41,6 +41,7 @@ static void prepare_lds_kernels() {
         (void)FwdCfg::prepare<false, true, EPI_BF16>();
         (void)FwdCfg::prepare<false, true, EPI_BF16_DGELU>();
         (void)DwCfg::prepare<true, true, EPI_F32>();
+        (void)DwCfg::prepare_dw_group();
     });
 }
 
@@ -148,4 +149,25 @@ void gemm_bf16_bwd_dw(float* dw, float* db, const bf16* dout, const bf16* inp, i
     launch(ws, splits, kchunk, n, db ? wsdb : nullptr, N);
     split_reduce_kernel<<<ceil_div(n / 4, 256), 256, 0, st>>>(dw, ws, splits, n);
     if (db) split_reduce_kernel<<<ceil_div(N / 4, 256), 256, 0, st>>>(db, wsdb, splits, N);
+}
+
+// Grouped weight gradients (see matmul_bwd_dw_batch); false (nothing
+// launched) when M is not a multiple of the tile depth.
+bool gemm_bf16_bwd_dw_batch(const DwTask* tasks, int n, int M, hipStream_t st) {
+    if (M % LDS_BK != 0) return false;
+    prepare_lds_kernels();
+    for (int t0 = 0; t0 < n; t0 += GROUP_MAX) {
+        DwGroup g;
+        g.count = n - t0 < GROUP_MAX ? n - t0 : GROUP_MAX;
+        g.R = M;
+        g.first_tile[0] = 0;
+        for (int q = 0; q < g.count; q++) {
+            const DwTask& t = tasks[t0 + q];
+            g.p[q] = DwProblem{(const bf16*)t.dout, (const bf16*)t.inp, t.dw, t.db, t.N, t.K};
+            g.first_tile[q + 1] =
+                g.first_tile[q] + ceil_div(t.N, DwCfg::bm) * ceil_div(t.K, DwCfg::bn);
+        }
+        DwCfg::run_dw_group(g, st);
+    }
+    return true;
 }

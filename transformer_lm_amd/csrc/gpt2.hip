@@ -133,9 +133,14 @@ void plan(const gpt2_config* c, Layout* lay) {
     a[A_LOSSES] = BT * 4;
     a[A_LOSS] = 4;
     a[A_ERR] = 4;
-    a[W_DRES] = a[W_DC] = BT * C * es;
-    a[W_D3C] = BT * 3 * C * es;
-    a[W_D4C] = BT * 4 * C * es;
+    // backward: the residual-stream gradient at every layer boundary (2L + 1
+    // of them) and the per-layer qkv / fc output gradients stay resident, so
+    // the weight gradients of all layers can run as one grouped product after
+    // the layer loop
+    a[W_DRES] = (2 * L + 1) * BT * C * es;
+    a[W_DC] = BT * C * es;
+    a[W_D3C] = L * BT * 3 * C * es;
+    a[W_D4C] = L * BT * 4 * C * es;
     a[W_ATT_D] = 2 * B * NH * T * 4;  // D, then the base-2 log-sum-exp
     a[W_LN_PART] = layernorm_bwd_partials((int)C) * 4;
     a[W_BIAS_PART] = bias_bwd_partials((int)BT, (int)(4 * C)) * 4;
@@ -366,10 +371,10 @@ void backward_impl(gpt2* h) {
     T* res3 = (T*)h->a[A_RESIDUAL3];
     T* lnf = (T*)h->a[A_LNF];
     T* dlogits = (T*)h->a[A_LOGITS];
-    T* dres = (T*)h->a[W_DRES];
+    T* dres = (T*)h->a[W_DRES];  // [2L + 1][BT][C]
     T* dC = (T*)h->a[W_DC];
-    T* d3C = (T*)h->a[W_D3C];
-    T* d4C = (T*)h->a[W_D4C];
+    T* d3C_all = (T*)h->a[W_D3C];  // [L][BT][3C]
+    T* d4C_all = (T*)h->a[W_D4C];  // [L][BT][4C]
     float* attD = (float*)h->a[W_ATT_D];
     float* lnp = (float*)h->a[W_LN_PART];
     float* bp = (float*)h->a[W_BIAS_PART];
@@ -377,6 +382,12 @@ void backward_impl(gpt2* h) {
     // LayerNorm backward reads x and dy, reads+writes (or writes) dx
     auto ln_bytes = [&](bool acc) { return (acc ? 4.0 : 3.0) * nC * es + 8.0 * BT + C * (es + 8); };
     const double attn_flops = 8.0 * B * NH * (C / NH) * causal_pairs(Tn);
+    // residual-stream gradient k: 0 = dLoss/d(output of the last block), then
+    // alternately d/d(x1) and d/d(input) of blocks L-1, L-2, ..., 0
+    auto R = [&](int k) { return dres + (int64_t)k * nC; };
+    std::vector<DwTask> dw_tasks;
+    dw_tasks.reserve(4 * L);
+    double dw_flops = 0.0;
 
     // output head (tied to wte): dlnf = dz . wte; dwte = dz^T . lnf
     {
@@ -389,27 +400,29 @@ void backward_impl(gpt2* h) {
     }
     {
         KScope k(h, K_LAYERNORM_BWD, ln_bytes(false));
-        layernorm_bwd<T>(dres, 0, G[P_LNFW], G[P_LNFB], dC, res3 + (L - 1) * nC, P[P_LNFW],
+        layernorm_bwd<T>(R(0), nullptr, G[P_LNFW], G[P_LNFB], dC, res3 + (L - 1) * nC, P[P_LNFW],
                          (float*)h->a[A_LNF_MEAN], (float*)h->a[A_LNF_RSTD], BT, C, lnp, st);
     }
     for (int l = L - 1; l >= 0; l--) {
         const T* res = l == 0 ? encoded : res3 + (l - 1) * nC;
         const int64_t w4 = (int64_t)l * 4 * C * C;
-        // MLP: dres is dLoss/d(x2), also the gradient of fcproj's output
+        const int kx = 2 * (L - 1 - l);
+        T* g2 = R(kx);      // dLoss/d(x2): the gradient of fcproj's output
+        T* g1 = R(kx + 1);  // dLoss/d(x1): the gradient of attproj's output
+        T* g0 = R(kx + 2);  // dLoss/d(block input)
+        T* d4C = d4C_all + (int64_t)l * 4 * nC;
+        T* d3C = d3C_all + (int64_t)l * 3 * nC;
+        // MLP
         if (std::is_same<T, bf16>::value) {
             // bf16: gelu' is applied in the product's epilogue
             KScope k(h, K_MATMUL_BWD_DX, mm_flops(BT, 4 * C, C));
-            matmul_bwd_dx_dgelu<T>(d4C, dres, P[P_FCPROJW] + w4, fch + l * 4 * nC, BT, C, 4 * C,
-                                   st);
+            matmul_bwd_dx_dgelu<T>(d4C, g2, P[P_FCPROJW] + w4, fch + l * 4 * nC, BT, C, 4 * C, st);
         } else {
             KScope k(h, K_MATMUL_BWD_DX, mm_flops(BT, 4 * C, C));
-            matmul_bwd_dx<T>(d4C, dres, P[P_FCPROJW] + w4, BT, C, 4 * C, st);
+            matmul_bwd_dx<T>(d4C, g2, P[P_FCPROJW] + w4, BT, C, 4 * C, st);
         }
-        {
-            KScope k(h, K_MATMUL_BWD_DW, mm_flops(C, 4 * C, BT));
-            matmul_bwd_dw<T>(G[P_FCPROJW] + w4, G[P_FCPROJB] + l * C, dres, fchg + l * 4 * nC, BT,
-                             C, 4 * C, dws, bp, st);
-        }
+        dw_tasks.push_back({g2, fchg + l * 4 * nC, G[P_FCPROJW] + w4, G[P_FCPROJB] + l * C, C,
+                            4 * C});
         if (!std::is_same<T, bf16>::value) {
             KScope k(h, K_GELU_BWD, 3.0 * 4 * nC * es);
             gelu_bwd<T>(d4C, fch + l * 4 * nC, d4C, 4 * nC, st);
@@ -418,28 +431,20 @@ void backward_impl(gpt2* h) {
             KScope k(h, K_MATMUL_BWD_DX, mm_flops(BT, C, 4 * C));
             matmul_bwd_dx<T>(dC, d4C, P[P_FCW] + w4, BT, 4 * C, C, st);
         }
-        {
-            KScope k(h, K_MATMUL_BWD_DW, mm_flops(4 * C, C, BT));
-            matmul_bwd_dw<T>(G[P_FCW] + w4, G[P_FCB] + l * 4 * C, d4C, ln2 + l * nC, BT, 4 * C, C,
-                             dws, bp, st);
-        }
+        dw_tasks.push_back({d4C, ln2 + l * nC, G[P_FCW] + w4, G[P_FCB] + l * 4 * C, 4 * C, C});
         {
             KScope k(h, K_LAYERNORM_BWD, ln_bytes(true));
-            layernorm_bwd<T>(dres, 1, G[P_LN2W] + l * C, G[P_LN2B] + l * C, dC, res2 + l * nC,
+            layernorm_bwd<T>(g1, g2, G[P_LN2W] + l * C, G[P_LN2B] + l * C, dC, res2 + l * nC,
                              P[P_LN2W] + l * C, ln2m + (int64_t)l * BT, ln2r + (int64_t)l * BT,
                              BT, C, lnp, st);
         }
-        // attention: dres is now dLoss/d(x1), also the gradient of attproj's output
+        // attention
         const int64_t w1 = (int64_t)l * C * C, w3 = (int64_t)l * 3 * C * C;
         {
             KScope k(h, K_MATMUL_BWD_DX, mm_flops(BT, C, C));
-            matmul_bwd_dx<T>(dC, dres, P[P_ATTPROJW] + w1, BT, C, C, st);
+            matmul_bwd_dx<T>(dC, g1, P[P_ATTPROJW] + w1, BT, C, C, st);
         }
-        {
-            KScope k(h, K_MATMUL_BWD_DW, mm_flops(C, C, BT));
-            matmul_bwd_dw<T>(G[P_ATTPROJW] + w1, G[P_ATTPROJB] + l * C, dres, atty + l * nC, BT, C,
-                             C, dws, bp, st);
-        }
+        dw_tasks.push_back({g1, atty + l * nC, G[P_ATTPROJW] + w1, G[P_ATTPROJB] + l * C, C, C});
         {
             KScope k(h, K_ATTENTION_BWD, attn_flops);
             attention_bwd<T>(d3C, dC, qkv + l * 3 * nC, atty + l * nC,
@@ -449,21 +454,23 @@ void backward_impl(gpt2* h) {
             KScope k(h, K_MATMUL_BWD_DX, mm_flops(BT, C, 3 * C));
             matmul_bwd_dx<T>(dC, d3C, P[P_QKVW] + w3, BT, 3 * C, C, st);
         }
-        {
-            KScope k(h, K_MATMUL_BWD_DW, mm_flops(3 * C, C, BT));
-            matmul_bwd_dw<T>(G[P_QKVW] + w3, G[P_QKVB] + l * 3 * C, d3C, ln1 + l * nC, BT, 3 * C,
-                             C, dws, bp, st);
-        }
+        dw_tasks.push_back({d3C, ln1 + l * nC, G[P_QKVW] + w3, G[P_QKVB] + l * 3 * C, 3 * C, C});
         {
             KScope k(h, K_LAYERNORM_BWD, ln_bytes(true));
-            layernorm_bwd<T>(dres, 1, G[P_LN1W] + l * C, G[P_LN1B] + l * C, dC, res,
+            layernorm_bwd<T>(g0, g1, G[P_LN1W] + l * C, G[P_LN1B] + l * C, dC, res,
                              P[P_LN1W] + l * C, ln1m + (int64_t)l * BT, ln1r + (int64_t)l * BT,
                              BT, C, lnp, st);
         }
+        dw_flops += mm_flops(C, 4 * C, BT) + mm_flops(4 * C, C, BT) + mm_flops(C, C, BT) +
+                    mm_flops(3 * C, C, BT);
+    }
+    {
+        KScope k(h, K_MATMUL_BWD_DW, dw_flops);
+        matmul_bwd_dw_batch<T>(dw_tasks.data(), (int)dw_tasks.size(), BT, dws, bp, st);
     }
     {
         KScope k(h, K_ENCODER_BWD, nC * es + 4.0 * c.max_T * C + 8.0 * BT);
-        encoder_bwd<T>(G[P_WTE], G[P_WPE], dres, h->last_inputs, B, Tn, C, Vp, c.max_T,
+        encoder_bwd<T>(G[P_WTE], G[P_WPE], R(2 * L), h->last_inputs, B, Tn, C, Vp, c.max_T,
                        h->a[W_ENC], st);
     }
 }

@@ -24,10 +24,11 @@ void encoder_bwd(float* dwte, float* dwpe, const T* dout, const int32_t* tok, in
 template <typename T>
 void layernorm_fwd(T* out, float* mean, float* rstd, const T* inp, const T* w, const T* b,
                    int N, int C, hipStream_t st);
-// dinp (+)= dx (accumulate != 0 adds); dw, db are written (fp32).
-// partials: fp32 workspace of layernorm_bwd_partials(C) floats.
+// dinp = dx (+ dadd[...] when dadd != nullptr; dadd may alias dinp); dw, db
+// are written (fp32). partials: fp32 workspace of layernorm_bwd_partials(C)
+// floats.
 template <typename T>
-void layernorm_bwd(T* dinp, int accumulate, float* dw, float* db, const T* dout, const T* inp,
+void layernorm_bwd(T* dinp, const T* dadd, float* dw, float* db, const T* dout, const T* inp,
                    const T* w, const float* mean, const float* rstd, int N, int C,
                    float* partials, hipStream_t st);
 int64_t layernorm_bwd_partials(int C);
@@ -71,6 +72,23 @@ int64_t gemm_dw_workspace_floats(int M, int N, int K);
 template <typename T>
 void bias_bwd(float* db, const T* dout, int M, int N, float* partials, hipStream_t st);
 int64_t bias_bwd_partials(int M, int N);
+
+// A batch of independent weight gradients over the same M rows:
+// dw_t[N_t, K_t] = dout_t[M, N_t]^T . inp_t[M, K_t] (fp32, written) and
+// db_t[N_t] = sum_m dout_t[m, :] when db_t != nullptr. bf16 storage runs them
+// as grouped launches of up to 64 products without reduction splits (M a
+// multiple of 64); otherwise one matmul_bwd_dw per task with ws / partials.
+struct DwTask {
+    const void* dout;
+    const void* inp;
+    float* dw;
+    float* db;
+    int N, K;
+};
+template <typename T>
+void matmul_bwd_dw_batch(const DwTask* tasks, int n, int M, float* ws, float* bias_partials,
+                         hipStream_t st);
+bool gemm_bf16_bwd_dw_batch(const DwTask* tasks, int n, int M, hipStream_t st);
 
 // ---- attention ---------------------------------------------------------------
 // Causal multi-head attention on qkv (B,T,3C): out (B,T,C), lse (B,NH,T).

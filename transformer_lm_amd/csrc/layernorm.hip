@@ -86,7 +86,7 @@ void layernorm_fwd(T* out, float* mean, float* rstd, const T* inp, const T* w, c
 
 template <typename T, int NCH>
 __global__ __launch_bounds__(256) void layernorm_bwd_kernel(
-    T* dinp, int accumulate, const T* __restrict__ dout, const T* __restrict__ inp,
+    T* dinp, const T* dadd, const T* __restrict__ dout, const T* __restrict__ inp,
     const T* __restrict__ w, const float* __restrict__ mean, const float* __restrict__ rstd,
     int N, int C, float* __restrict__ partials) {
     __shared__ float red[2 * 2048];
@@ -127,11 +127,11 @@ __global__ __launch_bounds__(256) void layernorm_bwd_kernel(
             const int c = (lane + 64 * k) * 8;
             if (c < C) {
                 float o[8];
-                if (accumulate) load8(dinp + (int64_t)row * C + c, o);
+                if (dadd) load8(dadd + (int64_t)row * C + c, o);
 #pragma unroll
                 for (int i = 0; i < 8; i++) {
                     const float dx = (wv[k][i] * dy[k][i] - gm - xh[k][i] * gxm) * r;
-                    o[i] = accumulate ? o[i] + dx : dx;
+                    o[i] = dadd ? o[i] + dx : dx;
                 }
                 store8(dinp + (int64_t)row * C + c, o);
             }
@@ -199,16 +199,16 @@ __global__ __launch_bounds__(256) void layernorm_bwd_reduce2_kernel(
 int64_t layernorm_bwd_partials(int C) { return (int64_t)(LN_BWD_BLOCKS + LN_RED_GROUPS) * 2 * C; }
 
 template <typename T>
-void layernorm_bwd(T* dinp, int accumulate, float* dw, float* db, const T* dout, const T* inp,
+void layernorm_bwd(T* dinp, const T* dadd, float* dw, float* db, const T* dout, const T* inp,
                    const T* w, const float* mean, const float* rstd, int N, int C,
                    float* partials, hipStream_t st) {
     int nb = ceil_div(N, LN_ROWS_PER_BLOCK);
     if (nb > LN_BWD_BLOCKS) nb = LN_BWD_BLOCKS;
     if (C <= 1024)
-        layernorm_bwd_kernel<T, 2><<<nb, 256, 0, st>>>(dinp, accumulate, dout, inp, w, mean, rstd,
+        layernorm_bwd_kernel<T, 2><<<nb, 256, 0, st>>>(dinp, dadd, dout, inp, w, mean, rstd,
                                                        N, C, partials);
     else
-        layernorm_bwd_kernel<T, 4><<<nb, 256, 0, st>>>(dinp, accumulate, dout, inp, w, mean, rstd,
+        layernorm_bwd_kernel<T, 4><<<nb, 256, 0, st>>>(dinp, dadd, dout, inp, w, mean, rstd,
                                                        N, C, partials);
     float* stage = partials + (int64_t)LN_BWD_BLOCKS * 2 * C;
     layernorm_bwd_reduce1_kernel<<<dim3(ceil_div(2 * C, 64), LN_RED_GROUPS), 256, 0, st>>>(
@@ -220,9 +220,9 @@ template void layernorm_fwd<float>(float*, float*, float*, const float*, const f
                                    const float*, int, int, hipStream_t);
 template void layernorm_fwd<bf16>(bf16*, float*, float*, const bf16*, const bf16*, const bf16*,
                                   int, int, hipStream_t);
-template void layernorm_bwd<float>(float*, int, float*, float*, const float*, const float*,
+template void layernorm_bwd<float>(float*, const float*, float*, float*, const float*, const float*,
                                    const float*, const float*, const float*, int, int, float*,
                                    hipStream_t);
-template void layernorm_bwd<bf16>(bf16*, int, float*, float*, const bf16*, const bf16*,
+template void layernorm_bwd<bf16>(bf16*, const bf16*, float*, float*, const bf16*, const bf16*,
                                   const bf16*, const float*, const float*, int, int, float*,
                                   hipStream_t);

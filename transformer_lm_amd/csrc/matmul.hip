@@ -150,6 +150,16 @@ void matmul_bwd_dw(float* dw, float* db, const T* dout, const T* inp, int M, int
     }
 }
 
+template <typename T>
+void matmul_bwd_dw_batch(const DwTask* tasks, int n, int M, float* ws, float* bias_partials,
+                         hipStream_t st) {
+    if constexpr (std::is_same<T, bf16>::value)
+        if (gemm_bf16_bwd_dw_batch(tasks, n, M, st)) return;
+    for (int i = 0; i < n; i++)
+        matmul_bwd_dw<T>(tasks[i].dw, tasks[i].db, (const T*)tasks[i].dout,
+                         (const T*)tasks[i].inp, M, tasks[i].N, tasks[i].K, ws, bias_partials, st);
+}
+
 // Bias gradient db[n] = sum_m dout[m, n], deterministic two-stage column sum.
 // Stage 1: a block covers 256 columns (32 threads x 8 columns, 16-byte loads)
 // and BB_ROWS rows split over 8 row phases; the phases are combined in order
@@ -214,6 +224,7 @@ void bias_bwd(float* db, const T* dout, int M, int N, float* partials, hipStream
                                          hipStream_t);                                         \
     template void matmul_bwd_dw<T>(float*, float*, const T*, const T*, int, int, int, float*,  \
                                    float*, hipStream_t);                                       \
-    template void bias_bwd<T>(float*, const T*, int, int, float*, hipStream_t);
+    template void bias_bwd<T>(float*, const T*, int, int, float*, hipStream_t);                \
+    template void matmul_bwd_dw_batch<T>(const DwTask*, int, int, float*, float*, hipStream_t);
 INST(float)
 INST(bf16)
