@@ -15,9 +15,11 @@
 #define GELU_C 0.044715f
 #define GELU_M2LOG2E (-2.8853900817779268f)  // -2 log2(e)
 
+// 1 / (1 + 2^(x (c1 + c2 x^2))) with c1 = -2 log2(e) sqrt(2/pi), c2 = 0.044715 c1
 __device__ __forceinline__ float gelu_sigmoid_2a(float x) {
-    const float a = GELU_K * fmaf(GELU_C * x, x * x, x);
-    return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(GELU_M2LOG2E * a));
+    constexpr float c1 = GELU_M2LOG2E * GELU_K, c2 = c1 * GELU_C;
+    const float u = x * fmaf(c2, x * x, c1);
+    return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(u));
 }
 
 __device__ __forceinline__ float gelu_fast(float x) { return x * gelu_sigmoid_2a(x); }

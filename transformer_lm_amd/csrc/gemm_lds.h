@@ -148,268 +148,321 @@ struct LdsOperand {
     }
 };
 
-// With rowsum != nullptr, the blocks of the first column tile also sum each X
-// row over their reduction range (for dW = dy^T x: the bias gradient).
-// One output tile (tm, tn) over reduction split z (rows z*kchunk ..).
-template <int BM, int BN, int BK, int WM, int WN, int GM, int S, bool XRC, bool YRC, int EPI>
-__device__ __forceinline__ void gemm_lds_tile(
-    void* __restrict__ out_, bf16* __restrict__ out2, const bf16* __restrict__ X,
-    const bf16* __restrict__ Y, const bf16* __restrict__ bias, const bf16* __restrict__ residual,
-    int M, int N, int K, int ldx, int ldy, int ldo, int kchunk, int64_t split_stride,
-    float* __restrict__ rowsum, int64_t rowsum_stride, int tm, int tn, int z) {
-    constexpr int NW = WM * WN, NT = NW * 64;
+// ---------------------------------------------------------------------------
+// Persistent grouped kernel. A launch runs a group of products of one layout
+// and epilogue ("problems": the layers' weight gradients, the reduction splits
+// of one weight gradient, or a single product). Problem q computes
+//   out_q[i, j] = sum_{p < K_q} X_q(i, p) Y_q(j, p),  i < M_q, j < N_q,
+// with row strides ldx = XRC ? M : K, ldy = YRC ? N : K, ldo = N, and, when
+// rowsum_q != nullptr, rowsum_q[i] = sum_p X_q(i, p) (the bias gradient of a
+// weight gradient).
+//
+// The tiles of all problems form one list; block b walks tiles b, b + G, ...
+// (G = grid size, two blocks per CU), each round handed to the XCDs in
+// contiguous ranges. The two-stage LDS ring runs on across tiles: while a
+// block computes the last k-step of one tile, the first stage of its next tile
+// is already loading, and that tile's products start while the stores of the
+// previous epilogue drain (the epilogue issues a fixed number of buffer stores
+// per lane, out-of-range ones dropped by the buffer range check, so the wait
+// for the prefetched stage can leave exactly those stores in flight).
+#define GROUP_MAX 48
+struct GemmProblem {
+    const bf16* X;
+    const bf16* Y;
+    void* out;             // bf16 (fp32 for EPI_F32), row stride N
+    bf16* out2;            // EPI_BF16_GELU: gelu(out)
+    const bf16* bias;      // EPI_BF16 / GELU: added per column (or nullptr)
+    const bf16* aux;       // EPI_BF16: residual (or nullptr); EPI_BF16_DGELU: pre-activation
+    float* rowsum;         // or nullptr
+    int M, N, K;
+};
+struct GemmGroup {
+    int count;
+    int first_tile[GROUP_MAX + 1];  // prefix sums of the problems' tile counts
+    GemmProblem p[GROUP_MAX];
+};
+
+#if __HIP_DEVICE_COMPILE__
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t store_rsrc(void* base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(base, 0, (int)min(bytes, (int64_t)0x7fffffff),
+                                             0x00020000);
+}
+#endif
+
+template <int BM, int BN, int BK, int WM, int WN, int GM, bool XRC, bool YRC, int EPI>
+__global__ __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_eu(2))) void gemm_persistent_kernel(const GemmGroup g) {
+#if __HIP_DEVICE_COMPILE__  // buffer builtins exist for the device pass only
+    constexpr int S = 2;
+    constexpr int NW = WM * WN;
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int FM = TM / 32, FN = TN / 32;
     static_assert(FM * 32 == TM && FN * 32 == TN, "wave tiles are whole 32x32 MFMA tiles");
     using XO = LdsOperand<BM, BK, NW, XRC>;
     using YO = LdsOperand<BN, BK, NW, YRC>;
-    constexpr int NPW = XO::NPW + YO::NPW;  // load instructions per wave per stage
+    constexpr int SLOT = XO::ELEMS + YO::ELEMS;  // one ring slot: [X tile][Y tile]
+    // buffer stores per lane per tile (the epilogue issues all of them)
+    constexpr int NST = EPI == EPI_F32 ? FN * (TM * 8 / 64)
+                        : EPI == EPI_BF16_GELU ? 2 * FN * (TM * 4 / 64) : FN * (TM * 4 / 64);
+    static_assert(NST < 64, "vmcnt range");
+    constexpr int SP = 36;  // staged row stride in floats (32 + 4: spreads banks)
+    static_assert(NW * TM * SP * 4 <= SLOT * 2, "staging fits in one ring slot");
     extern __shared__ __attribute__((aligned(16))) bf16 lds_ring[];
-    bf16* Xs = lds_ring;                  // [S][BM * BK]
-    bf16* Ys = lds_ring + S * XO::ELEMS;  // [S][BN * BK]
 
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int wm = wid % WM, wn = wid / WM;
-    const int i0 = tm * BM, j0 = tn * BN;
-    const int kbeg = z * kchunk;
-    const int nk = (min(K, kbeg + kchunk) - kbeg) / BK;
+    const int fr = lane & 31, g4 = lane >> 5;
+    const int total = g.first_tile[g.count];
+    const int G = gridDim.x;
 
-    floatx16 acc[FN][FM];
-#pragma unroll
-    for (int a = 0; a < FN; a++)
-#pragma unroll
-        for (int b = 0; b < FM; b++) acc[a][b] = floatx16{};
+    // tile of iteration `it` (XCD-contiguous ranges inside every full round)
+    auto tile_at = [&](int it) {
+        const int r0 = it - (int)blockIdx.x;
+        if (r0 + G <= total && G % NUM_XCD == 0)
+            return r0 + ((int)blockIdx.x % NUM_XCD) * (G / NUM_XCD) + (int)blockIdx.x / NUM_XCD;
+        return it;
+    };
+    int q = 0;
+    auto decode = [&](int t, int& tm, int& tn) {
+        while (q + 1 < g.count && g.first_tile[q + 1] <= t) q++;
+        const GemmProblem& pr = g.p[q];
+        const int nbm = (pr.M + BM - 1) / BM, nbn = (pr.N + BN - 1) / BN;
+        const int lt = t - g.first_tile[q];
+        const int gsz = GM * nbn, grp = lt / gsz, first = grp * GM;
+        const int rows = min(GM, nbm - first), r = lt - grp * gsz;
+        tm = first + r % rows;
+        tn = r / rows;
+    };
 
+    int it = blockIdx.x;
+    if (it >= total) return;
+    int tm, tn;
+    decode(tile_at(it), tm, tn);
+    int qc = q;
     XO xo;
     YO yo;
-    xo.init(ldx, M, i0, wid, lane);
-    yo.init(ldy, N, j0, wid, lane);
-#pragma unroll
-    for (int s = 0; s < S - 1; s++)
-        if (s < nk) {
-            xo.load(Xs + s * XO::ELEMS, X, ldx, i0, kbeg + s * BK, wid);
-            yo.load(Ys + s * YO::ELEMS, Y, ldy, j0, kbeg + s * BK, wid);
-        }
-
-    const bool do_rowsum = rowsum != nullptr && tn == 0 && tid < BM;
-    float rsum = 0.f;
-    const int fr = lane & 31, g = lane >> 5;
-    for (int kt = 0; kt < nk; kt++) {
-        const int pending = min(S - 2, nk - 1 - kt);
-        if (pending >= 3) wait_vmcnt<3 * NPW>();
-        else if (pending == 2) wait_vmcnt<2 * NPW>();
-        else if (pending == 1) wait_vmcnt<NPW>();
-        else wait_vmcnt<0>();
-        // This wave's reads of the buffer refilled below finished before its
-        // last MFMA of the previous step consumed them.
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        if (kt + S - 1 < nk) {
-            const int sn = (kt + S - 1) % S;
-            xo.load(Xs + sn * XO::ELEMS, X, ldx, i0, kbeg + (kt + S - 1) * BK, wid);
-            yo.load(Ys + sn * YO::ELEMS, Y, ldy, j0, kbeg + (kt + S - 1) * BK, wid);
-        }
-        const bf16* xb = Xs + (kt % S) * XO::ELEMS;
-        const bf16* yb = Ys + (kt % S) * YO::ELEMS;
-        if (do_rowsum)
-#pragma unroll 8
-            for (int k = 0; k < BK; k++) rsum += XO::at(xb, tid, k);
-        bf16x8 a[2][FN], b[2][FM];
-        auto read_frags = [&](int kk, bf16x8* af, bf16x8* bfr) {
-#pragma unroll
-            for (int f = 0; f < FN; f++) af[f] = YO::frag(yb, wn * TN + f * 32, kk, lane);
-#pragma unroll
-            for (int f = 0; f < FM; f++) bfr[f] = XO::frag(xb, wm * TM + f * 32, kk, lane);
-        };
-        read_frags(0, a[0], b[0]);
-#pragma unroll
-        for (int kk = 0; kk < BK / 16; kk++) {
-            // Fragments of step kk+1 are requested before the products of
-            // step kk; the scheduling fences keep the compiler from sinking
-            // each read next to its first use (which would expose the LDS
-            // latency before every product).
-            if (kk + 1 < BK / 16) read_frags(kk + 1, a[(kk + 1) & 1], b[(kk + 1) & 1]);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int fn = 0; fn < FN; fn++)
-#pragma unroll
-                for (int fm = 0; fm < FM; fm++)
-                    acc[fn][fm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        a[kk & 1][fn], b[kk & 1][fm], acc[fn][fm], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
-        }
+    {
+        const GemmProblem& pr = g.p[qc];
+        xo.init(XRC ? pr.M : pr.K, pr.M, tm * BM, wid, lane);
+        yo.init(YRC ? pr.N : pr.K, pr.N, tn * BN, wid, lane);
+        xo.load(lds_ring, pr.X, XRC ? pr.M : pr.K, tm * BM, 0, wid);
+        yo.load(lds_ring + XO::ELEMS, pr.Y, YRC ? pr.N : pr.K, tn * BN, 0, wid);
     }
-    if (do_rowsum && i0 + tid < M) rowsum[z * rowsum_stride + i0 + tid] = rsum;
-    (void)NT;
-    // Pin the accumulators to AGPRs: otherwise the bf16 epilogue's conversions
-    // pull them into VGPRs for the whole kernel, and wide wave tiles spill.
-#pragma unroll
-    for (int fn = 0; fn < FN; fn++)
-#pragma unroll
-        for (int fm = 0; fm < FM; fm++) asm volatile("" : "+a"(acc[fn][fm]));
+    int slot = 0;
+    bool first = true;
+    while (true) {
+        const GemmProblem& pr = g.p[qc];
+        const int M = pr.M, N = pr.N, K = pr.K;
+        const int ldx = XRC ? M : K, ldy = YRC ? N : K, ldo = N;
+        const int i0 = tm * BM, j0 = tn * BN;
+        const int nk = K / BK;
+        const int it_next = it + G;
+        const bool has_next = it_next < total;
+        int tm_n = 0, tn_n = 0;
+        if (has_next) decode(tile_at(it_next), tm_n, tn_n);
+        const int qn = q;
 
-    // Epilogue through LDS, one 32-column slice of the wave tile at a time: a
-    // lane holds output row i = l%32 of each 32x32 tile and columns in runs of
-    // 4, so direct stores would write 16 bytes to 32 rows per instruction.
-    // Staged as fp32 rows, the slice leaves as 64-byte (bf16) or 128-byte
-    // (fp32) contiguous row segments; bias and residual are read the same way
-    // and added in fp32 before the single rounding.
-    constexpr int SP = 36;  // staged row stride in floats (32 + 4: spreads banks)
-    static_assert(NW * TM * SP * 4 <= S * (BM + BN) * BK * 2, "staging fits in the ring");
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();  // every wave is done reading the ring
-    float* stage = reinterpret_cast<float*>(lds_ring) + wid * (TM * SP);
-    const int ib = i0 + wm * TM;
+        floatx16 acc[FN][FM];
 #pragma unroll
-    for (int fn = 0; fn < FN; fn++) {
+        for (int a = 0; a < FN; a++)
 #pragma unroll
-        for (int fm = 0; fm < FM; fm++)
+            for (int b = 0; b < FM; b++) acc[a][b] = floatx16{};
+        const bool do_rowsum = pr.rowsum != nullptr && tn == 0 && tid < BM;
+        float rsum = 0.f;
+
+        // Epilogue inputs: the bias and residual / pre-activation of slice 0
+        // are requested with the last k-step (their latency hides behind its
+        // products), those of slice fn+1 before the stores of slice fn (a load
+        // issued after stores could only be waited for together with them:
+        // the counter is in order).
+        constexpr bool HAS_BIAS = EPI == EPI_BF16_B || EPI == EPI_BF16_BR || EPI == EPI_BF16_GELU;
+        constexpr bool HAS_AUX = EPI == EPI_BF16_R || EPI == EPI_BF16_BR || EPI == EPI_BF16_DGELU;
+        constexpr int NIT = TM * 4 / 64;  // bf16 store rounds per slice
+        const int cl = (lane & 3) * 8;    // this lane's column offset in a slice
+        bf16x8 auxv[2][NIT], biasv[2];
+        auto fetch = [&](int fn, int buf) {
+            const int jb = j0 + wn * TN + fn * 32;
+            const int j = min(jb + cl, N - 8);  // clamped: out-of-range values are unused
+            if (HAS_BIAS) biasv[buf] = *reinterpret_cast<const bf16x8*>(pr.bias + j);
+            if (HAS_AUX)
 #pragma unroll
-            for (int q = 0; q < 4; q++)
-                *reinterpret_cast<floatx4*>(stage + (fm * 32 + fr) * SP + 8 * q + 4 * g) =
-                    floatx4{acc[fn][fm][4 * q], acc[fn][fm][4 * q + 1], acc[fn][fm][4 * q + 2],
-                            acc[fn][fm][4 * q + 3]};
-        // a wave's LDS accesses are processed in order: its reads below see
-        // these writes, and the next slice's writes follow these reads
-        const int jb = j0 + wn * TN + fn * 32;
-        if (EPI == EPI_F32) {
-#pragma unroll
-            for (int it = 0; it < TM * 8 / 64; it++) {
-                const int idx = it * 64 + lane, r = idx >> 3, c = (idx & 7) * 4;
-                const int i = ib + r, j = jb + c;
-                if (i < M && j < N)
-                    *reinterpret_cast<floatx4*>(reinterpret_cast<float*>(out_) +
-                                                z * split_stride + (int64_t)i * ldo + j) =
-                        *reinterpret_cast<const floatx4*>(stage + r * SP + c);
+                for (int itr = 0; itr < NIT; itr++) {
+                    const int i = min(i0 + wm * TM + ((itr * 64 + lane) >> 2), M - 1);
+                    auxv[buf][itr] = *reinterpret_cast<const bf16x8*>(pr.aux + (int64_t)i * ldo + j);
+                }
+        };
+        for (int kt = 0; kt < nk; kt++) {
+            // this stage's loads were the last ones issued, except right after
+            // an epilogue, whose NST stores followed them
+            if (kt == 0 && !first) wait_vmcnt<NST>();
+            else wait_vmcnt<0>();
+            // this wave's reads of the slot refilled below finished before its
+            // last MFMA of the previous step consumed them
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            bf16* nxt = lds_ring + (slot ^ 1) * SLOT;
+            if (kt + 1 < nk) {
+                xo.load(nxt, pr.X, ldx, i0, (kt + 1) * BK, wid);
+                yo.load(nxt + XO::ELEMS, pr.Y, ldy, j0, (kt + 1) * BK, wid);
+            } else if (has_next) {
+                const GemmProblem& pn = g.p[qn];
+                XO xn;
+                YO yn;
+                xn.init(XRC ? pn.M : pn.K, pn.M, tm_n * BM, wid, lane);
+                yn.init(YRC ? pn.N : pn.K, pn.N, tn_n * BN, wid, lane);
+                xn.load(nxt, pn.X, XRC ? pn.M : pn.K, tm_n * BM, 0, wid);
+                yn.load(nxt + XO::ELEMS, pn.Y, YRC ? pn.N : pn.K, tn_n * BN, 0, wid);
+                xo = xn;
+                yo = yn;
             }
-        } else {
+            if ((HAS_BIAS || HAS_AUX) && kt + 1 == nk) fetch(0, 0);
+            const bf16* xb = lds_ring + slot * SLOT;
+            const bf16* yb = xb + XO::ELEMS;
+            if (do_rowsum)
+#pragma unroll 8
+                for (int k = 0; k < BK; k++) rsum += XO::at(xb, tid, k);
+            bf16x8 a[2][FN], b[2][FM];
+            auto read_frags = [&](int kk, bf16x8* af, bf16x8* bfr) {
 #pragma unroll
-            for (int it = 0; it < TM * 4 / 64; it++) {
-                const int idx = it * 64 + lane, r = idx >> 2, c = (idx & 3) * 8;
-                const int i = ib + r, j = jb + c;
-                if (i < M && j < N) {
-                    const floatx4 lo = *reinterpret_cast<const floatx4*>(stage + r * SP + c);
-                    const floatx4 hi = *reinterpret_cast<const floatx4*>(stage + r * SP + c + 4);
+                for (int f = 0; f < FN; f++) af[f] = YO::frag(yb, wn * TN + f * 32, kk, lane);
+#pragma unroll
+                for (int f = 0; f < FM; f++) bfr[f] = XO::frag(xb, wm * TM + f * 32, kk, lane);
+            };
+            read_frags(0, a[0], b[0]);
+#pragma unroll
+            for (int kk = 0; kk < BK / 16; kk++) {
+                // fragments of step kk+1 are requested before the products of
+                // step kk; the fences keep the compiler from sinking each read
+                // next to its first use
+                if (kk + 1 < BK / 16) read_frags(kk + 1, a[(kk + 1) & 1], b[(kk + 1) & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int fn = 0; fn < FN; fn++)
+#pragma unroll
+                    for (int fm = 0; fm < FM; fm++)
+                        acc[fn][fm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            a[kk & 1][fn], b[kk & 1][fm], acc[fn][fm], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            slot ^= 1;
+        }
+        if (do_rowsum && i0 + tid < M) pr.rowsum[i0 + tid] = rsum;
+        // Pin the accumulators to AGPRs: otherwise the bf16 epilogue's
+        // conversions pull them into VGPRs for the whole kernel.
+#pragma unroll
+        for (int fn = 0; fn < FN; fn++)
+#pragma unroll
+            for (int fm = 0; fm < FM; fm++) asm volatile("" : "+a"(acc[fn][fm]));
+
+        // Epilogue through LDS (in the slot just consumed; the other one holds
+        // the next tile's first stage), one 32-column slice of the wave tile at
+        // a time: a lane holds output row l%32 of each 32x32 tile and columns
+        // in runs of 4, so direct stores would write 16 bytes to 32 rows per
+        // instruction. Staged as fp32 rows, the slice leaves as 64-byte (bf16)
+        // or 128-byte (fp32) row segments; bias, residual and pre-activation
+        // are read the same way and applied in fp32 before the single rounding.
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();  // every wave is done with the slot
+        float* stage = reinterpret_cast<float*>(lds_ring + (slot ^ 1) * SLOT) + wid * (TM * SP);
+        const int ib = i0 + wm * TM;
+        constexpr int ES = EPI == EPI_F32 ? 4 : 2;
+        const int64_t rows_left = min(BM, M - i0) - wm * TM;  // may be <= 0
+        const int64_t span = rows_left > 0 ? rows_left * ldo * ES : 0;
+        char* obase = reinterpret_cast<char*>(pr.out) + ((int64_t)ib * ldo) * ES;
+        const auto rs_out = store_rsrc(obase, span);
+        const auto rs_out2 =
+            store_rsrc(EPI == EPI_BF16_GELU ? reinterpret_cast<char*>(pr.out2) + (int64_t)ib * ldo * 2
+                                            : obase,
+                       span);
+#pragma unroll
+        for (int fn = 0; fn < FN; fn++) {
+#pragma unroll
+            for (int fm = 0; fm < FM; fm++)
+#pragma unroll
+                for (int qq = 0; qq < 4; qq++)
+                    *reinterpret_cast<floatx4*>(stage + (fm * 32 + fr) * SP + 8 * qq + 4 * g4) =
+                        floatx4{acc[fn][fm][4 * qq], acc[fn][fm][4 * qq + 1],
+                                acc[fn][fm][4 * qq + 2], acc[fn][fm][4 * qq + 3]};
+            if ((HAS_BIAS || HAS_AUX) && fn + 1 < FN) fetch(fn + 1, (fn + 1) & 1);
+            // a wave's LDS accesses are processed in order: its reads below see
+            // these writes, and the next slice's writes follow these reads
+            const int jb = j0 + wn * TN + fn * 32;
+            if (EPI == EPI_F32) {
+#pragma unroll
+                for (int itr = 0; itr < TM * 8 / 64; itr++) {
+                    const int idx = itr * 64 + lane, r = idx >> 3, c = (idx & 7) * 4;
+                    const int j = jb + c;
+                    const uint32_t off = j < N ? (uint32_t)((r * ldo + j) * 4) : 0x80000000u;
+                    const floatx4 v = *reinterpret_cast<const floatx4*>(stage + r * SP + c);
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs_out, off,
+                                                           0, 0);
+                }
+            } else {
+#pragma unroll
+                for (int itr = 0; itr < NIT; itr++) {
+                    const int r = (itr * 64 + lane) >> 2;
+                    const int j = jb + cl;
+                    const floatx4 lo = *reinterpret_cast<const floatx4*>(stage + r * SP + cl);
+                    const floatx4 hi = *reinterpret_cast<const floatx4*>(stage + r * SP + cl + 4);
                     float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                    if (bias) {
-                        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(bias + j);
+                    if (HAS_BIAS)
 #pragma unroll
-                        for (int e = 0; e < 8; e++) v[e] += (float)bv[e];
-                    }
-                    if (EPI == EPI_BF16 && residual) {
-                        const bf16x8 rv =
-                            *reinterpret_cast<const bf16x8*>(residual + (int64_t)i * ldo + j);
+                        for (int e = 0; e < 8; e++) v[e] += (float)biasv[fn & 1][e];
+                    if (EPI == EPI_BF16_R || EPI == EPI_BF16_BR)
 #pragma unroll
-                        for (int e = 0; e < 8; e++) v[e] += (float)rv[e];
-                    }
-                    if (EPI == EPI_BF16_DGELU) {
-                        const bf16x8 xv =
-                            *reinterpret_cast<const bf16x8*>(residual + (int64_t)i * ldo + j);
+                        for (int e = 0; e < 8; e++) v[e] += (float)auxv[fn & 1][itr][e];
+                    if (EPI == EPI_BF16_DGELU)
 #pragma unroll
-                        for (int e = 0; e < 8; e++) v[e] *= gelu_grad_fast((float)xv[e]);
-                    }
+                        for (int e = 0; e < 8; e++)
+                            v[e] *= gelu_grad_fast((float)auxv[fn & 1][itr][e]);
                     bf16x8 o;
 #pragma unroll
                     for (int e = 0; e < 8; e++) o[e] = (bf16)v[e];
-                    *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(out_) + (int64_t)i * ldo +
-                                               j) = o;
+                    const uint32_t off = j < N ? (uint32_t)((r * ldo + j) * 2) : 0x80000000u;
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), rs_out, off,
+                                                           0, 0);
                     if (EPI == EPI_BF16_GELU) {
                         bf16x8 ga;
 #pragma unroll
                         for (int e = 0; e < 8; e++) ga[e] = (bf16)gelu_fast((float)o[e]);
-                        *reinterpret_cast<bf16x8*>(out2 + (int64_t)i * ldo + j) = ga;
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ga),
+                                                               rs_out2, off, 0, 0);
                     }
                 }
             }
         }
+        if (!has_next) break;
+        it = it_next;
+        qc = qn;
+        tm = tm_n;
+        tn = tn_n;
+        first = false;
     }
+    (void)S;
+#endif
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int GM, int S, bool XRC, bool YRC, int EPI>
-__global__ __launch_bounds__(WM* WN * 64) void gemm_lds_kernel(
-    void* __restrict__ out_, bf16* __restrict__ out2, const bf16* __restrict__ X,
-    const bf16* __restrict__ Y, const bf16* __restrict__ bias, const bf16* __restrict__ residual,
-    int M, int N, int K, int ldx, int ldy, int ldo, int kchunk, int64_t split_stride,
-    float* __restrict__ rowsum, int64_t rowsum_stride) {
-    int tm, tn;
-    tile_of<GM>(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
-    gemm_lds_tile<BM, BN, BK, WM, WN, GM, S, XRC, YRC, EPI>(
-        out_, out2, X, Y, bias, residual, M, N, K, ldx, ldy, ldo, kchunk, split_stride, rowsum,
-        rowsum_stride, tm, tn, blockIdx.z);
-}
-
-// A batch of independent weight-gradient products dw_p[N_p, K_p] (fp32) =
-// dout_p[R, N_p]^T . inp_p[R, K_p] over the same R rows, with db_p[N_p] = the
-// column sums of dout_p when db_p != nullptr, in one launch: the tiles of all
-// problems form one grid (no reduction splits), handed to the XCDs in
-// contiguous ranges.
-#define GROUP_MAX 64
-struct DwProblem {
-    const bf16* dout;
-    const bf16* inp;
-    float* dw;
-    float* db;
-    int N, K;
-};
-struct DwGroup {
-    int count, R;
-    int first_tile[GROUP_MAX + 1];  // prefix sums of the problems' tile counts
-    DwProblem p[GROUP_MAX];
-};
-
-template <int BM, int BN, int BK, int WM, int WN, int GM, int S>
-__global__ __launch_bounds__(WM* WN * 64) void gemm_lds_dw_group_kernel(const DwGroup g) {
-    const int total = g.first_tile[g.count];
-    const int per = total / NUM_XCD;
-    int t = blockIdx.x;
-    if (t < per * NUM_XCD) t = (t % NUM_XCD) * per + t / NUM_XCD;
-    int q = 0;
-    while (q + 1 < g.count && g.first_tile[q + 1] <= t) q++;
-    const DwProblem& pr = g.p[q];
-    const int nbm = (pr.N + BM - 1) / BM, nbn = (pr.K + BN - 1) / BN;
-    const int lt = t - g.first_tile[q];
-    // GM-row groups walked column by column, as in tile_of
-    const int gsz = GM * nbn, grp = lt / gsz, first = grp * GM;
-    const int rows = min(GM, nbm - first), r = lt - grp * gsz;
-    const int tm = first + r % rows, tn = r / rows;
-    gemm_lds_tile<BM, BN, BK, WM, WN, GM, S, true, true, EPI_F32>(
-        pr.dw, nullptr, pr.dout, pr.inp, nullptr, nullptr, pr.N, pr.K, g.R, pr.N, pr.K, pr.K,
-        g.R, 0, pr.db, 0, tm, tn, 0);
-}
-
-template <int BM, int BN, int BK, int WM, int WN, int GM, int S>
+// Launch helper for one tile shape: the grid is min(total tiles, two blocks
+// per CU).
+template <int BM, int BN, int BK, int WM, int WN, int GM>
 struct GemmLds {
     static constexpr int bm = BM, bn = BN, bk = BK;
-    static constexpr size_t lds_bytes = (size_t)S * (BM + BN) * BK * sizeof(bf16);
+    static constexpr size_t lds_bytes = (size_t)2 * (BM + BN) * BK * sizeof(bf16);
+
+    static int tiles(int M, int N) { return ceil_div(M, BM) * ceil_div(N, BN); }
 
     template <bool XRC, bool YRC, int EPI>
-    static void run(void* out, const bf16* X, const bf16* Y, const bf16* bias,
-                    const bf16* residual, int M, int N, int K, int ldx, int ldy, int ldo,
-                    int splits, int kchunk, int64_t split_stride, float* rowsum,
-                    int64_t rowsum_stride, hipStream_t st, bf16* out2 = nullptr) {
-        const int tiles = ceil_div(M, BM) * ceil_div(N, BN);
-        dim3 grid(tiles, 1, splits);
-        gemm_lds_kernel<BM, BN, BK, WM, WN, GM, S, XRC, YRC, EPI>
-            <<<grid, WM * WN * 64, lds_bytes, st>>>(out, out2, X, Y, bias, residual, M, N, K, ldx,
-                                                    ldy, ldo, kchunk, split_stride, rowsum,
-                                                    rowsum_stride);
-    }
-
-    static void run_dw_group(const DwGroup& g, hipStream_t st) {
-        gemm_lds_dw_group_kernel<BM, BN, BK, WM, WN, GM, S>
-            <<<g.first_tile[g.count], WM * WN * 64, lds_bytes, st>>>(g);
-    }
-
-    static hipError_t prepare_dw_group() {
-        return hipFuncSetAttribute((const void*)gemm_lds_dw_group_kernel<BM, BN, BK, WM, WN, GM, S>,
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
+    static void run(const GemmGroup& g, hipStream_t st) {
+        const int total = g.first_tile[g.count];
+        const int grid = total < 2 * 256 ? total : 2 * 256;
+        gemm_persistent_kernel<BM, BN, BK, WM, WN, GM, XRC, YRC, EPI>
+            <<<grid, WM * WN * 64, lds_bytes, st>>>(g);
     }
 
     // Raises the kernel's dynamic-LDS limit (needed above 64 KB); call once.
     template <bool XRC, bool YRC, int EPI>
     static hipError_t prepare() {
         return hipFuncSetAttribute(
-            (const void*)gemm_lds_kernel<BM, BN, BK, WM, WN, GM, S, XRC, YRC, EPI>,
+            (const void*)gemm_persistent_kernel<BM, BN, BK, WM, WN, GM, XRC, YRC, EPI>,
             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
     }
 };

@@ -93,11 +93,22 @@ struct Stager {
     }
 };
 
-// EPI_BF16: out bf16 = acc (+ bias) (+ residual);  EPI_F32: out fp32 = acc.
-// Direct-to-LDS kernel only: EPI_BF16_GELU: out = bf16(acc + bias), out2 =
+// EPI_BF16: out bf16 = acc (+ bias) (+ residual), the terms present when
+// their pointers are non-null (in the persistent kernel: neither term);
+// EPI_F32: out fp32 = acc. Persistent kernel only, with the terms fixed at
+// compile time: EPI_BF16_B: + bias; EPI_BF16_R: + residual; EPI_BF16_BR:
+// + bias + residual; EPI_BF16_GELU: out = bf16(acc + bias), out2 =
 // bf16(gelu(out)); EPI_BF16_DGELU: out = bf16(acc * gelu'(aux)) with aux the
-// bf16 pre-activation (passed as `residual`).
-enum { EPI_BF16 = 0, EPI_F32 = 1, EPI_BF16_GELU = 2, EPI_BF16_DGELU = 3 };
+// bf16 pre-activation.
+enum {
+    EPI_BF16 = 0,
+    EPI_F32 = 1,
+    EPI_BF16_GELU = 2,
+    EPI_BF16_DGELU = 3,
+    EPI_BF16_B = 4,
+    EPI_BF16_R = 5,
+    EPI_BF16_BR = 6
+};
 
 // Tile coordinates of block `bid` of `total` = nbm x nbn tiles (see the file
 // comment): XCD-contiguous ranges, GM-row groups walked column by column.
