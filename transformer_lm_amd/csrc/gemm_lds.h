@@ -59,8 +59,53 @@ __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Buffer resource over the bytes at base (gfx9 raw buffer, no range limit
-// beyond 4 GB offsets; every offset used here stays far below that).
+// Direct global -> LDS loads (buffer_load ... lds), issued through inline asm.
+// Issued as builtins, the compiler counts them and then makes every transpose
+// read (ds_read_b64_tr_b16) wait for all of them, since it cannot tell which
+// LDS bytes that read touches; that would drain the prefetch each k-step.
+// Hidden from it, they are covered by the pipelines' explicit vmcnt waits; the
+// compiler's own waits for other loads stay safe, as they count a subset of
+// the operations in flight (a wait for "at most n outstanding" then leaves
+// fewer, never more, incomplete). The instructions write no registers.
+//
+// Raw buffer resource (gfx9 layout): base, stride 0, num_records, dword 3,
+// made wave-uniform (it lives in scalar registers).
+__device__ __forceinline__ u32x4 raw_rsrc(const void* base) {
+    const uint64_t a = (uint64_t)base;
+    return u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a),
+                 (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu),
+                 0x7fffffffu, 0x00020000u};
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)__builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p);
+}
+
+// 16 bytes per lane from rsrc + soff + voff to LDS at lds + lane * 16 (lds is
+// wave-uniform). M0, bound as an input, carries the LDS address; the leading
+// s_nop gives the one wait state the hardware needs between writing M0 and
+// the load that reads it. No memory clobber: the loads stay ordered against
+// the pipelines' waits and barriers (volatile asm and barrier intrinsics,
+// which do fence memory), while the compiler may schedule LDS reads of other
+// ring slots around them.
+__device__ __forceinline__ void lds_dma16(u32x4 rs, uint32_t voff, uint32_t soff, const void* lds) {
+#if __HIP_DEVICE_COMPILE__
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                 :
+                 : "v"(voff), "s"(rs), "s"(soff), "{m0}"(lds_addr(lds)));
+#endif
+}
+
+// 4 bytes per lane, to lds + lane * 4.
+__device__ __forceinline__ void lds_dma4(u32x4 rs, uint32_t voff, uint32_t soff, const void* lds) {
+#if __HIP_DEVICE_COMPILE__
+    asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, %2 offen lds"
+                 :
+                 : "v"(voff), "s"(rs), "s"(soff), "{m0}"(lds_addr(lds)));
+#endif
+}
+
 #if __HIP_DEVICE_COMPILE__
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_at(const void* base) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, 0x00020000);
@@ -70,7 +115,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_at(const void* base) {
 // One operand tile (ROWS x BK) of the ring: its loads and fragment reads.
 // Loads are MUBUF buffer_load ... lds: unlike the FLAT-encoded global form,
 // they leave the compiler's LDS wait counting exact, so fragment reads can
-// stay in flight across matrix products.
+// stay in flight across matrix products (see lds_dma16).
 template <int ROWS, int BK, int NW, bool RC>
 struct LdsOperand {
     static constexpr int CHUNKS = ROWS * BK / 8;  // 16-byte chunks per tile
@@ -101,20 +146,33 @@ struct LdsOperand {
         }
     }
 
-    // Loads the tile at rows row0.., reduction k0.. into LDS at s.
+    // Loads the tile at rows row0.., reduction k0.. into LDS at s, through
+    // inline asm (ASM) or the compiler builtin. Measured: the asm form helps
+    // the dx layout (reduction-contiguous X, transpose-read Y), the builtin
+    // form the forward and weight-gradient layouts.
+    template <bool ASM>
     __device__ __forceinline__ void load(bf16* s, const bf16* __restrict__ g, int ld, int row0,
                                          int k0, int wid) const {
-#if __HIP_DEVICE_COMPILE__  // the buffer builtins exist for the device pass only
         const bf16* base = RC ? g + (int64_t)k0 * ld + row0 : g + (int64_t)row0 * ld + k0;
-        const auto rs = buffer_at(base);
+        if constexpr (ASM) {
+            const u32x4 rs = raw_rsrc(base);
 #pragma unroll
-        for (int j = 0; j < NPW; j++) {
-            const int blk = min(wid * NPW + j, TOTAL - 1);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rs, (__attribute__((address_space(3))) void*)(s + blk * 512), 16, voff[j], 0, 0,
-                0);
-        }
+            for (int j = 0; j < NPW; j++) {
+                const int blk = min(wid * NPW + j, TOTAL - 1);
+                lds_dma16(rs, voff[j], 0, s + blk * 512);
+            }
+        } else {
+#if __HIP_DEVICE_COMPILE__
+            const auto rs = buffer_at(base);
+#pragma unroll
+            for (int j = 0; j < NPW; j++) {
+                const int blk = min(wid * NPW + j, TOTAL - 1);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rs, (__attribute__((address_space(3))) void*)(s + blk * 512), 16, voff[j], 0,
+                    0, 0);
+            }
 #endif
+        }
     }
 
     // MFMA fragment of tile rows r0..r0+31, reduction block kk (16 wide).
@@ -206,6 +264,7 @@ __global__ __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_eu(2))
     static_assert(NST < 64, "vmcnt range");
     constexpr int SP = 36;  // staged row stride in floats (32 + 4: spreads banks)
     static_assert(NW * TM * SP * 4 <= SLOT * 2, "staging fits in one ring slot");
+    constexpr bool ASM = !XRC && YRC;  // see LdsOperand::load
     extern __shared__ __attribute__((aligned(16))) bf16 lds_ring[];
 
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -244,8 +303,8 @@ __global__ __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_eu(2))
         const GemmProblem& pr = g.p[qc];
         xo.init(XRC ? pr.M : pr.K, pr.M, tm * BM, wid, lane);
         yo.init(YRC ? pr.N : pr.K, pr.N, tn * BN, wid, lane);
-        xo.load(lds_ring, pr.X, XRC ? pr.M : pr.K, tm * BM, 0, wid);
-        yo.load(lds_ring + XO::ELEMS, pr.Y, YRC ? pr.N : pr.K, tn * BN, 0, wid);
+        xo.template load<ASM>(lds_ring, pr.X, XRC ? pr.M : pr.K, tm * BM, 0, wid);
+        yo.template load<ASM>(lds_ring + XO::ELEMS, pr.Y, YRC ? pr.N : pr.K, tn * BN, 0, wid);
     }
     int slot = 0;
     bool first = true;
@@ -301,16 +360,16 @@ __global__ __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_eu(2))
             __builtin_amdgcn_s_barrier();
             bf16* nxt = lds_ring + (slot ^ 1) * SLOT;
             if (kt + 1 < nk) {
-                xo.load(nxt, pr.X, ldx, i0, (kt + 1) * BK, wid);
-                yo.load(nxt + XO::ELEMS, pr.Y, ldy, j0, (kt + 1) * BK, wid);
+                xo.template load<ASM>(nxt, pr.X, ldx, i0, (kt + 1) * BK, wid);
+                yo.template load<ASM>(nxt + XO::ELEMS, pr.Y, ldy, j0, (kt + 1) * BK, wid);
             } else if (has_next) {
                 const GemmProblem& pn = g.p[qn];
                 XO xn;
                 YO yn;
                 xn.init(XRC ? pn.M : pn.K, pn.M, tm_n * BM, wid, lane);
                 yn.init(YRC ? pn.N : pn.K, pn.N, tn_n * BN, wid, lane);
-                xn.load(nxt, pn.X, XRC ? pn.M : pn.K, tm_n * BM, 0, wid);
-                yn.load(nxt + XO::ELEMS, pn.Y, YRC ? pn.N : pn.K, tn_n * BN, 0, wid);
+                xn.template load<ASM>(nxt, pn.X, XRC ? pn.M : pn.K, tm_n * BM, 0, wid);
+                yn.template load<ASM>(nxt + XO::ELEMS, pn.Y, YRC ? pn.N : pn.K, tn_n * BN, 0, wid);
                 xo = xn;
                 yo = yn;
             }

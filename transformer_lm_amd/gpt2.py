@@ -11,7 +11,9 @@ import os
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libgpt2.so")
+# GPT2_LIB selects another build of the same library (side-by-side timing of
+# two builds in one process tree); the default is the in-tree build.
+LIB_PATH = os.environ.get("GPT2_LIB") or os.path.join(HERE, "libgpt2.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run transformer_lm_amd.build.build() "
