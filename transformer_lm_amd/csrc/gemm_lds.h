@@ -224,6 +224,10 @@ struct LdsOperand {
 // per lane, out-of-range ones dropped by the buffer range check, so the wait
 // for the prefetched stage can leave exactly those stores in flight).
 #define GROUP_MAX 48
+// Cache policy of the epilogue's buffer stores: non-temporal (nt), so the
+// written outputs do not displace the operand panels that the L2 serves to
+// the other tiles.
+#define ST_NT 2
 struct GemmProblem {
     const bf16* X;
     const bf16* Y;
@@ -453,7 +457,7 @@ __global__ __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_eu(2))
                     const uint32_t off = j < N ? (uint32_t)((r * ldo + j) * 4) : 0x80000000u;
                     const floatx4 v = *reinterpret_cast<const floatx4*>(stage + r * SP + c);
                     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs_out, off,
-                                                           0, 0);
+                                                           0, ST_NT);
                 }
             } else {
 #pragma unroll
@@ -478,13 +482,13 @@ __global__ __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_eu(2))
                     for (int e = 0; e < 8; e++) o[e] = (bf16)v[e];
                     const uint32_t off = j < N ? (uint32_t)((r * ldo + j) * 2) : 0x80000000u;
                     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), rs_out, off,
-                                                           0, 0);
+                                                           0, ST_NT);
                     if (EPI == EPI_BF16_GELU) {
                         bf16x8 ga;
 #pragma unroll
                         for (int e = 0; e < 8; e++) ga[e] = (bf16)gelu_fast((float)o[e]);
                         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ga),
-                                                               rs_out2, off, 0, 0);
+                                                               rs_out2, off, 0, ST_NT);
                     }
                 }
             }
