@@ -147,9 +147,8 @@ struct LdsOperand {
     }
 
     // Loads the tile at rows row0.., reduction k0.. into LDS at s, through
-    // inline asm (ASM) or the compiler builtin. Measured: the asm form helps
-    // the dx layout (reduction-contiguous X, transpose-read Y), the builtin
-    // form the forward and weight-gradient layouts.
+    // inline asm (ASM) or the compiler builtin (see gemm_stream_kernel for
+    // which layout uses which).
     template <bool ASM>
     __device__ __forceinline__ void load(bf16* s, const bf16* __restrict__ g, int ld, int row0,
                                          int k0, int wid) const {
@@ -197,32 +196,24 @@ struct LdsOperand {
         }
     }
 
-    // Element (row r, reduction index k) of the staged tile.
-    __device__ __forceinline__ static float at(const bf16* s, int r, int k) {
-        if constexpr (!RC)
-            return (float)s[r * BK + ((((k >> 3) ^ pc_swz<BK>(r))) << 3) + (k & 7)];
-        else
-            return (float)s[k * ROWS + (((r >> 3) ^ rc_swz<ROWS>(k)) << 3) + (r & 7)];
-    }
 };
 
 // ---------------------------------------------------------------------------
-// Persistent grouped kernel. A launch runs a group of products of one layout
-// and epilogue ("problems": the layers' weight gradients, the reduction splits
-// of one weight gradient, or a single product). Problem q computes
+// Persistent grouped streaming kernel. A launch runs a group of products of
+// one layout and epilogue ("problems": the layers' weight gradients, the
+// reduction splits of one weight gradient, or a single product). Problem q
+// computes
 //   out_q[i, j] = sum_{p < K_q} X_q(i, p) Y_q(j, p),  i < M_q, j < N_q,
 // with row strides ldx = XRC ? M : K, ldy = YRC ? N : K, ldo = N, and, when
 // rowsum_q != nullptr, rowsum_q[i] = sum_p X_q(i, p) (the bias gradient of a
 // weight gradient).
 //
 // The tiles of all problems form one list; block b walks tiles b, b + G, ...
-// (G = grid size, two blocks per CU), each round handed to the XCDs in
-// contiguous ranges. The two-stage LDS ring runs on across tiles: while a
-// block computes the last k-step of one tile, the first stage of its next tile
-// is already loading, and that tile's products start while the stores of the
-// previous epilogue drain (the epilogue issues a fixed number of buffer stores
-// per lane, out-of-range ones dropped by the buffer range check, so the wait
-// for the prefetched stage can leave exactly those stores in flight).
+// (G = grid size: OCC blocks per CU), each round of G tiles handed to the XCDs
+// in contiguous ranges. The k-steps of a block's tiles form one stream: a load
+// cursor runs S-1 stages ahead of the products, across tile boundaries, so the
+// next tile's first stages load while the current tile finishes and while its
+// epilogue drains.
 #define GROUP_MAX 48
 // Cache policy of the epilogue's buffer stores: non-temporal (nt), so the
 // written outputs do not displace the operand panels that the L2 serves to
@@ -233,8 +224,8 @@ struct GemmProblem {
     const bf16* Y;
     void* out;             // bf16 (fp32 for EPI_F32), row stride N
     bf16* out2;            // EPI_BF16_GELU: gelu(out)
-    const bf16* bias;      // EPI_BF16 / GELU: added per column (or nullptr)
-    const bf16* aux;       // EPI_BF16: residual (or nullptr); EPI_BF16_DGELU: pre-activation
+    const bf16* bias;      // EPI_BF16_B / BR / GELU: added per column
+    const bf16* aux;       // EPI_BF16_R / BR: residual; EPI_BF16_DGELU: pre-activation
     float* rowsum;         // or nullptr
     int M, N, K;
 };
@@ -251,24 +242,54 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t store_rsrc(void* base, int64_t
 }
 #endif
 
-template <int BM, int BN, int BK, int WM, int WN, int GM, bool XRC, bool YRC, int EPI>
-__global__ __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_eu(2))) void gemm_persistent_kernel(const GemmGroup g) {
+// Barrier after this wave's LDS reads and writes have completed. As one asm
+// statement with a memory clobber, no memory access moves across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Wait counts. vmcnt counts a lane's vector-memory operations (loads and
+// stores alike) in issue order, and "vmcnt(n)" waits until at most n are
+// outstanding; any n not above the number of operations issued after the
+// awaited stage's loads is safe. In steady state S-2 stages (LPS load
+// instructions each) follow the awaited one; after an epilogue its NST
+// buffer stores follow too, for the S-1 steps whose loads preceded them. Near
+// the end of the block's stream fewer stages follow: everything is awaited.
+// Inline-asm loads are invisible to the compiler, whose own waits (for the
+// epilogue's bias and residual loads) then count a subset of the operations in
+// flight and stay safe.
+template <int BM, int BN, int BK, int WM, int WN, int GM, int S, int OCC, bool XRC, bool YRC,
+          int EPI>
+__global__ __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_eu(OCC * WM * WN / 4)))
+void gemm_stream_kernel(const GemmGroup g) {
 #if __HIP_DEVICE_COMPILE__  // buffer builtins exist for the device pass only
-    constexpr int S = 2;
     constexpr int NW = WM * WN;
+    constexpr int NT = NW * 64;
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int FM = TM / 32, FN = TN / 32;
     static_assert(FM * 32 == TM && FN * 32 == TN, "wave tiles are whole 32x32 MFMA tiles");
+    static_assert(S >= 2, "ring depth");
     using XO = LdsOperand<BM, BK, NW, XRC>;
     using YO = LdsOperand<BN, BK, NW, YRC>;
     constexpr int SLOT = XO::ELEMS + YO::ELEMS;  // one ring slot: [X tile][Y tile]
-    // buffer stores per lane per tile (the epilogue issues all of them)
-    constexpr int NST = EPI == EPI_F32 ? FN * (TM * 8 / 64)
-                        : EPI == EPI_BF16_GELU ? 2 * FN * (TM * 4 / 64) : FN * (TM * 4 / 64);
-    static_assert(NST < 64, "vmcnt range");
+    constexpr int LPS = XO::NPW + YO::NPW;       // load instructions per lane per stage
+    constexpr bool HAS_BIAS = EPI == EPI_BF16_B || EPI == EPI_BF16_BR || EPI == EPI_BF16_GELU;
+    constexpr bool HAS_AUX = EPI == EPI_BF16_R || EPI == EPI_BF16_BR || EPI == EPI_BF16_DGELU;
+    // buffer stores per lane per 32x32 output sub-tile, and per tile
+    constexpr int SPT = EPI == EPI_F32 || EPI == EPI_BF16_GELU ? 4 : 2;
+    constexpr int NST = FN * FM * SPT;
+    constexpr int W_STEADY = (S - 2) * LPS;
+    constexpr int W_EPI = W_STEADY + NST < 63 ? W_STEADY + NST : 63;
+    static_assert(W_STEADY < 64, "vmcnt range");
     constexpr int SP = 36;  // staged row stride in floats (32 + 4: spreads banks)
-    static_assert(NW * TM * SP * 4 <= SLOT * 2, "staging fits in one ring slot");
-    constexpr bool ASM = !XRC && YRC;  // see LdsOperand::load
+    static_assert(NW * 32 * SP * 4 <= SLOT * 2, "sub-tile staging fits one ring slot");
+    constexpr int RSG = NT / (BM / 8);  // row sums: k groups of 16-byte column chunks
+    static_assert(!XRC || (BK % RSG == 0 && RSG * BM * 4 <= SLOT * 2), "row-sum layout");
+    // The transpose reads of the dx and dW layouts need the inline-asm loads:
+    // builtin loads make the compiler wait for all of them before every such
+    // read (it cannot tell which LDS bytes a read touches). The forward layout
+    // reads with ds_read_b128, which the compiler keeps apart from the loads.
+    constexpr bool ASM = YRC;
     extern __shared__ __attribute__((aligned(16))) bf16 lds_ring[];
 
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -276,6 +297,7 @@ __global__ __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_eu(2))
     const int fr = lane & 31, g4 = lane >> 5;
     const int total = g.first_tile[g.count];
     const int G = gridDim.x;
+    if ((int)blockIdx.x >= total) return;
 
     // tile of iteration `it` (XCD-contiguous ranges inside every full round)
     auto tile_at = [&](int it) {
@@ -284,8 +306,9 @@ __global__ __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_eu(2))
             return r0 + ((int)blockIdx.x % NUM_XCD) * (G / NUM_XCD) + (int)blockIdx.x / NUM_XCD;
         return it;
     };
-    int q = 0;
-    auto decode = [&](int t, int& tm, int& tn) {
+    // problem q (advanced monotonically) and tile coordinates of list tile t;
+    // within a problem, GM row tiles share each column of tiles
+    auto decode = [&](int t, int& q, int& tm, int& tn) {
         while (q + 1 < g.count && g.first_tile[q + 1] <= t) q++;
         const GemmProblem& pr = g.p[q];
         const int nbm = (pr.M + BM - 1) / BM, nbn = (pr.N + BN - 1) / BN;
@@ -296,228 +319,264 @@ __global__ __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_eu(2))
         tn = r / rows;
     };
 
-    int it = blockIdx.x;
-    if (it >= total) return;
-    int tm, tn;
-    decode(tile_at(it), tm, tn);
-    int qc = q;
-    XO xo;
-    YO yo;
-    {
-        const GemmProblem& pr = g.p[qc];
-        xo.init(XRC ? pr.M : pr.K, pr.M, tm * BM, wid, lane);
-        yo.init(YRC ? pr.N : pr.K, pr.N, tn * BN, wid, lane);
-        xo.template load<ASM>(lds_ring, pr.X, XRC ? pr.M : pr.K, tm * BM, 0, wid);
-        yo.template load<ASM>(lds_ring + XO::ELEMS, pr.Y, YRC ? pr.N : pr.K, tn * BN, 0, wid);
-    }
-    int slot = 0;
-    bool first = true;
-    while (true) {
-        const GemmProblem& pr = g.p[qc];
-        const int M = pr.M, N = pr.N, K = pr.K;
-        const int ldx = XRC ? M : K, ldy = YRC ? N : K, ldo = N;
-        const int i0 = tm * BM, j0 = tn * BN;
-        const int nk = K / BK;
-        const int it_next = it + G;
-        const bool has_next = it_next < total;
-        int tm_n = 0, tn_n = 0;
-        if (has_next) decode(tile_at(it_next), tm_n, tn_n);
-        const int qn = q;
-
-        floatx16 acc[FN][FM];
-#pragma unroll
-        for (int a = 0; a < FN; a++)
-#pragma unroll
-            for (int b = 0; b < FM; b++) acc[a][b] = floatx16{};
-        const bool do_rowsum = pr.rowsum != nullptr && tn == 0 && tid < BM;
-        float rsum = 0.f;
-
-        // Epilogue inputs: the bias and residual / pre-activation of slice 0
-        // are requested with the last k-step (their latency hides behind its
-        // products), those of slice fn+1 before the stores of slice fn (a load
-        // issued after stores could only be waited for together with them:
-        // the counter is in order).
-        constexpr bool HAS_BIAS = EPI == EPI_BF16_B || EPI == EPI_BF16_BR || EPI == EPI_BF16_GELU;
-        constexpr bool HAS_AUX = EPI == EPI_BF16_R || EPI == EPI_BF16_BR || EPI == EPI_BF16_DGELU;
-        constexpr int NIT = TM * 4 / 64;  // bf16 store rounds per slice
-        const int cl = (lane & 3) * 8;    // this lane's column offset in a slice
-        bf16x8 auxv[2][NIT], biasv[2];
-        auto fetch = [&](int fn, int buf) {
-            const int jb = j0 + wn * TN + fn * 32;
-            const int j = min(jb + cl, N - 8);  // clamped: out-of-range values are unused
-            if (HAS_BIAS) biasv[buf] = *reinterpret_cast<const bf16x8*>(pr.bias + j);
-            if (HAS_AUX)
-#pragma unroll
-                for (int itr = 0; itr < NIT; itr++) {
-                    const int i = min(i0 + wm * TM + ((itr * 64 + lane) >> 2), M - 1);
-                    auxv[buf][itr] = *reinterpret_cast<const bf16x8*>(pr.aux + (int64_t)i * ldo + j);
-                }
-        };
-        for (int kt = 0; kt < nk; kt++) {
-            // this stage's loads were the last ones issued, except right after
-            // an epilogue, whose NST stores followed them
-            if (kt == 0 && !first) wait_vmcnt<NST>();
-            else wait_vmcnt<0>();
-            // this wave's reads of the slot refilled below finished before its
-            // last MFMA of the previous step consumed them
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            __builtin_amdgcn_s_barrier();
-            bf16* nxt = lds_ring + (slot ^ 1) * SLOT;
-            if (kt + 1 < nk) {
-                xo.template load<ASM>(nxt, pr.X, ldx, i0, (kt + 1) * BK, wid);
-                yo.template load<ASM>(nxt + XO::ELEMS, pr.Y, ldy, j0, (kt + 1) * BK, wid);
-            } else if (has_next) {
-                const GemmProblem& pn = g.p[qn];
-                XO xn;
-                YO yn;
-                xn.init(XRC ? pn.M : pn.K, pn.M, tm_n * BM, wid, lane);
-                yn.init(YRC ? pn.N : pn.K, pn.N, tn_n * BN, wid, lane);
-                xn.template load<ASM>(nxt, pn.X, XRC ? pn.M : pn.K, tm_n * BM, 0, wid);
-                yn.template load<ASM>(nxt + XO::ELEMS, pn.Y, YRC ? pn.N : pn.K, tn_n * BN, 0, wid);
-                xo = xn;
-                yo = yn;
-            }
-            if ((HAS_BIAS || HAS_AUX) && kt + 1 == nk) fetch(0, 0);
-            const bf16* xb = lds_ring + slot * SLOT;
-            const bf16* yb = xb + XO::ELEMS;
-            if (do_rowsum)
-#pragma unroll 8
-                for (int k = 0; k < BK; k++) rsum += XO::at(xb, tid, k);
-            bf16x8 a[2][FN], b[2][FM];
-            auto read_frags = [&](int kk, bf16x8* af, bf16x8* bfr) {
-#pragma unroll
-                for (int f = 0; f < FN; f++) af[f] = YO::frag(yb, wn * TN + f * 32, kk, lane);
-#pragma unroll
-                for (int f = 0; f < FM; f++) bfr[f] = XO::frag(xb, wm * TM + f * 32, kk, lane);
-            };
-            read_frags(0, a[0], b[0]);
-#pragma unroll
-            for (int kk = 0; kk < BK / 16; kk++) {
-                // fragments of step kk+1 are requested before the products of
-                // step kk; the fences keep the compiler from sinking each read
-                // next to its first use
-                if (kk + 1 < BK / 16) read_frags(kk + 1, a[(kk + 1) & 1], b[(kk + 1) & 1]);
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int fn = 0; fn < FN; fn++)
-#pragma unroll
-                    for (int fm = 0; fm < FM; fm++)
-                        acc[fn][fm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            a[kk & 1][fn], b[kk & 1][fm], acc[fn][fm], 0, 0, 0);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            slot ^= 1;
+    // ---- load cursor
+    int l_it = blockIdx.x, l_kt = 0, l_q = 0, l_nk = 1, l_i0 = 0, l_j0 = 0;
+    bool l_on = true;
+    XO lx;
+    YO ly;
+    auto l_start = [&]() {
+        int tm, tn;
+        decode(tile_at(l_it), l_q, tm, tn);
+        const GemmProblem& p = g.p[l_q];
+        l_i0 = tm * BM;
+        l_j0 = tn * BN;
+        l_nk = p.K / BK;
+        lx.init(XRC ? p.M : p.K, p.M, l_i0, wid, lane);
+        ly.init(YRC ? p.N : p.K, p.N, l_j0, wid, lane);
+    };
+    l_start();
+    int issued = 0;  // stages issued so far
+    auto issue = [&](int slot) {
+        if (!l_on) return;
+        const GemmProblem& p = g.p[l_q];
+        bf16* dst = lds_ring + slot * SLOT;
+        lx.template load<ASM>(dst, p.X, XRC ? p.M : p.K, l_i0, l_kt * BK, wid);
+        ly.template load<ASM>(dst + XO::ELEMS, p.Y, YRC ? p.N : p.K, l_j0, l_kt * BK, wid);
+        issued++;
+        if (++l_kt == l_nk) {
+            l_kt = 0;
+            l_it += G;
+            l_on = l_it < total;
+            if (l_on) l_start();
         }
-        if (do_rowsum && i0 + tid < M) pr.rowsum[i0 + tid] = rsum;
-        // Pin the accumulators to AGPRs: otherwise the bf16 epilogue's
-        // conversions pull them into VGPRs for the whole kernel.
+    };
 #pragma unroll
-        for (int fn = 0; fn < FN; fn++)
-#pragma unroll
-            for (int fm = 0; fm < FM; fm++) asm volatile("" : "+a"(acc[fn][fm]));
+    for (int s = 0; s < S - 1; s++) issue(s);
 
-        // Epilogue through LDS (in the slot just consumed; the other one holds
-        // the next tile's first stage), one 32-column slice of the wave tile at
-        // a time: a lane holds output row l%32 of each 32x32 tile and columns
-        // in runs of 4, so direct stores would write 16 bytes to 32 rows per
-        // instruction. Staged as fp32 rows, the slice leaves as 64-byte (bf16)
-        // or 128-byte (fp32) row segments; bias, residual and pre-activation
-        // are read the same way and applied in fp32 before the single rounding.
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        __builtin_amdgcn_s_barrier();  // every wave is done with the slot
-        float* stage = reinterpret_cast<float*>(lds_ring + (slot ^ 1) * SLOT) + wid * (TM * SP);
-        const int ib = i0 + wm * TM;
-        constexpr int ES = EPI == EPI_F32 ? 4 : 2;
-        const int64_t rows_left = min(BM, M - i0) - wm * TM;  // may be <= 0
-        const int64_t span = rows_left > 0 ? rows_left * ldo * ES : 0;
-        char* obase = reinterpret_cast<char*>(pr.out) + ((int64_t)ib * ldo) * ES;
-        const auto rs_out = store_rsrc(obase, span);
-        const auto rs_out2 =
-            store_rsrc(EPI == EPI_BF16_GELU ? reinterpret_cast<char*>(pr.out2) + (int64_t)ib * ldo * 2
-                                            : obase,
-                       span);
+    // ---- compute cursor
+    int c_it = blockIdx.x, c_q = 0, c_tm, c_tn;
+    decode(tile_at(c_it), c_q, c_tm, c_tn);
+    int c_kt = 0, c_nk = g.p[c_q].K / BK;
+    int step = 0, epi_after = -1;  // stages issued before the last epilogue
+    int slot_c = 0, slot_l = S - 1;
+
+    floatx16 acc[FN][FM];
 #pragma unroll
-        for (int fn = 0; fn < FN; fn++) {
+    for (int a = 0; a < FN; a++)
 #pragma unroll
-            for (int fm = 0; fm < FM; fm++)
+        for (int b = 0; b < FM; b++) acc[a][b] = floatx16{};
+    // row sums: thread (rs_g, rs_c) adds chunk rs_c of k rows rs_g, rs_g + RSG, ...
+    float rs[8] = {};
+    const int rs_c = tid % (BM / 8), rs_g = tid / (BM / 8);
+
+    // epilogue inputs of sub-tile st (32x32, slice fn = st / FM): this lane's
+    // 8 columns of the slice (bias) and of the sub-tile's rows r, r + 16
+    // (residual / pre-activation), double-buffered. Those of the first
+    // sub-tile are requested with the tile's last k-step, each later one's
+    // before the stores of the one before.
+    const int cl = (lane & 3) * 8;
+    bf16x8 biasv[2], auxv[2][2];
+    auto fetch = [&](const GemmProblem& pr, int i0, int j0, int st) {
+        const int fn = st / FM, fm = st % FM, buf = st & 1;
+        const int j = min(j0 + wn * TN + fn * 32 + cl, pr.N - 8);
+        if (HAS_BIAS && fm == 0) biasv[fn & 1] = *reinterpret_cast<const bf16x8*>(pr.bias + j);
+        if (HAS_AUX)
+#pragma unroll
+            for (int itr = 0; itr < 2; itr++) {
+                const int i = min(i0 + wm * TM + fm * 32 + ((itr * 64 + lane) >> 2), pr.M - 1);
+                auxv[buf][itr] = *reinterpret_cast<const bf16x8*>(pr.aux + (int64_t)i * pr.N + j);
+            }
+    };
+
+    while (true) {
+        const int ahead = issued - step - 1;  // stages issued after this one
+        if (ahead >= S - 2) {
+            if (epi_after > step) wait_vmcnt<W_EPI>();
+            else wait_vmcnt<W_STEADY>();
+        } else {
+            wait_vmcnt<0>();
+        }
+        // every wave's loads of this stage have landed, and every wave is done
+        // reading the slot that the next load refills
+        lds_barrier();
+        const GemmProblem& pr = g.p[c_q];
+        if ((HAS_BIAS || HAS_AUX) && c_kt + 1 == c_nk) fetch(pr, c_tm * BM, c_tn * BN, 0);
+        issue(slot_l);
+
+        const bf16* xb = lds_ring + slot_c * SLOT;
+        const bf16* yb = xb + XO::ELEMS;
+        const bool do_rowsum = XRC && pr.rowsum != nullptr && c_tn == 0;
+        if constexpr (XRC) {
+            if (do_rowsum) {
+#pragma unroll
+                for (int k = rs_g; k < BK; k += RSG) {
+                    const bf16x8 v = *reinterpret_cast<const bf16x8*>(
+                        xb + k * BM + ((rs_c ^ rc_swz<BM>(k)) << 3));
+#pragma unroll
+                    for (int e = 0; e < 8; e++) rs[e] += (float)v[e];
+                }
+            }
+        }
+        bf16x8 a[2][FN], b[2][FM];
+        auto read_frags = [&](int kk, bf16x8* af, bf16x8* bfr) {
+#pragma unroll
+            for (int f = 0; f < FN; f++) af[f] = YO::frag(yb, wn * TN + f * 32, kk, lane);
+#pragma unroll
+            for (int f = 0; f < FM; f++) bfr[f] = XO::frag(xb, wm * TM + f * 32, kk, lane);
+        };
+        read_frags(0, a[0], b[0]);
+#pragma unroll
+        for (int kk = 0; kk < BK / 16; kk++) {
+            // fragments of step kk+1 are requested before the products of
+            // step kk; the fences keep the compiler from sinking each read
+            // next to its first use
+            if (kk + 1 < BK / 16) read_frags(kk + 1, a[(kk + 1) & 1], b[(kk + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int fn = 0; fn < FN; fn++)
+#pragma unroll
+                for (int fm = 0; fm < FM; fm++)
+                    acc[fn][fm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        a[kk & 1][fn], b[kk & 1][fm], acc[fn][fm], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+
+        if (++c_kt == c_nk) {
+            // ---- epilogue of tile (c_q, c_tm, c_tn), staged through LDS (the
+            // slot just consumed; the others hold the next stages) one 32x32
+            // sub-tile at a time: a lane holds output row l%32 of each MFMA
+            // tile and columns in runs of 4, so direct stores would write 16
+            // bytes to 32 rows per instruction. Staged as fp32 rows, a sub-tile
+            // leaves as 64-byte (bf16) or 128-byte (fp32) row segments; bias,
+            // residual and pre-activation are applied in fp32 before the one
+            // rounding.
+            // Pin the accumulators to AGPRs: otherwise the bf16 epilogue's
+            // conversions pull them into VGPRs for the whole kernel.
+#pragma unroll
+            for (int fn = 0; fn < FN; fn++)
+#pragma unroll
+                for (int fm = 0; fm < FM; fm++) asm volatile("" : "+a"(acc[fn][fm]));
+            const int M = pr.M, N = pr.N, ldo = N;
+            const int i0 = c_tm * BM, j0 = c_tn * BN;
+            lds_barrier();  // every wave is done with slot_c
+            float* sbase = reinterpret_cast<float*>(lds_ring + slot_c * SLOT);
+            if constexpr (XRC) {
+                if (do_rowsum) {
+                    // partial sums of the RSG k groups, added in group order
+#pragma unroll
+                    for (int e = 0; e < 8; e++) sbase[rs_g * BM + rs_c * 8 + e] = rs[e];
+                    lds_barrier();
+                    if (tid < BM && i0 + tid < M) {
+                        float t = 0.f;
+                        for (int q = 0; q < RSG; q++) t += sbase[q * BM + tid];
+                        pr.rowsum[i0 + tid] = t;
+                    }
+                    lds_barrier();
+#pragma unroll
+                    for (int e = 0; e < 8; e++) rs[e] = 0.f;
+                }
+            }
+            float* stage = sbase + wid * (32 * SP);
+            const int ib = i0 + wm * TM;
+            constexpr int ES = EPI == EPI_F32 ? 4 : 2;
+            const int64_t rows_left = min(BM, M - i0) - wm * TM;  // may be <= 0
+            const int64_t span = rows_left > 0 ? rows_left * ldo * ES : 0;
+            char* obase = reinterpret_cast<char*>(pr.out) + ((int64_t)ib * ldo) * ES;
+            const auto rs_out = store_rsrc(obase, span);
+            const auto rs_out2 =
+                store_rsrc(EPI == EPI_BF16_GELU ? reinterpret_cast<char*>(pr.out2) + (int64_t)ib * ldo * 2
+                                                : obase,
+                           span);
+#pragma unroll
+            for (int st = 0; st < FN * FM; st++) {
+                const int fn = st / FM, fm = st % FM;
 #pragma unroll
                 for (int qq = 0; qq < 4; qq++)
-                    *reinterpret_cast<floatx4*>(stage + (fm * 32 + fr) * SP + 8 * qq + 4 * g4) =
+                    *reinterpret_cast<floatx4*>(stage + fr * SP + 8 * qq + 4 * g4) =
                         floatx4{acc[fn][fm][4 * qq], acc[fn][fm][4 * qq + 1],
                                 acc[fn][fm][4 * qq + 2], acc[fn][fm][4 * qq + 3]};
-            if ((HAS_BIAS || HAS_AUX) && fn + 1 < FN) fetch(fn + 1, (fn + 1) & 1);
-            // a wave's LDS accesses are processed in order: its reads below see
-            // these writes, and the next slice's writes follow these reads
-            const int jb = j0 + wn * TN + fn * 32;
-            if (EPI == EPI_F32) {
+                if ((HAS_BIAS || HAS_AUX) && st + 1 < FN * FM) fetch(pr, i0, j0, st + 1);
+                // a wave's LDS accesses are processed in order: its reads below
+                // see these writes, and the next sub-tile's writes follow them
+                const int jb = j0 + wn * TN + fn * 32;
+                if constexpr (EPI == EPI_F32) {
 #pragma unroll
-                for (int itr = 0; itr < TM * 8 / 64; itr++) {
-                    const int idx = itr * 64 + lane, r = idx >> 3, c = (idx & 7) * 4;
-                    const int j = jb + c;
-                    const uint32_t off = j < N ? (uint32_t)((r * ldo + j) * 4) : 0x80000000u;
-                    const floatx4 v = *reinterpret_cast<const floatx4*>(stage + r * SP + c);
-                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs_out, off,
-                                                           0, ST_NT);
-                }
-            } else {
+                    for (int itr = 0; itr < 4; itr++) {
+                        const int idx = itr * 64 + lane, r = idx >> 3, c = (idx & 7) * 4;
+                        const int j = jb + c;
+                        const uint32_t off =
+                            j < N ? (uint32_t)(((fm * 32 + r) * ldo + j) * 4) : 0x80000000u;
+                        const floatx4 v = *reinterpret_cast<const floatx4*>(stage + r * SP + c);
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs_out,
+                                                               off, 0, ST_NT);
+                    }
+                } else {
 #pragma unroll
-                for (int itr = 0; itr < NIT; itr++) {
-                    const int r = (itr * 64 + lane) >> 2;
-                    const int j = jb + cl;
-                    const floatx4 lo = *reinterpret_cast<const floatx4*>(stage + r * SP + cl);
-                    const floatx4 hi = *reinterpret_cast<const floatx4*>(stage + r * SP + cl + 4);
-                    float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                    if (HAS_BIAS)
+                    for (int itr = 0; itr < 2; itr++) {
+                        const int r = (itr * 64 + lane) >> 2;
+                        const int j = jb + cl;
+                        const floatx4 lo = *reinterpret_cast<const floatx4*>(stage + r * SP + cl);
+                        const floatx4 hi = *reinterpret_cast<const floatx4*>(stage + r * SP + cl + 4);
+                        float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                        if constexpr (HAS_BIAS)
 #pragma unroll
-                        for (int e = 0; e < 8; e++) v[e] += (float)biasv[fn & 1][e];
-                    if (EPI == EPI_BF16_R || EPI == EPI_BF16_BR)
+                            for (int e = 0; e < 8; e++) v[e] += (float)biasv[fn & 1][e];
+                        if constexpr (EPI == EPI_BF16_R || EPI == EPI_BF16_BR)
 #pragma unroll
-                        for (int e = 0; e < 8; e++) v[e] += (float)auxv[fn & 1][itr][e];
-                    if (EPI == EPI_BF16_DGELU)
+                            for (int e = 0; e < 8; e++) v[e] += (float)auxv[st & 1][itr][e];
+                        if constexpr (EPI == EPI_BF16_DGELU)
 #pragma unroll
-                        for (int e = 0; e < 8; e++)
-                            v[e] *= gelu_grad_fast((float)auxv[fn & 1][itr][e]);
-                    bf16x8 o;
+                            for (int e = 0; e < 8; e++)
+                                v[e] *= gelu_grad_fast((float)auxv[st & 1][itr][e]);
+                        bf16x8 o;
 #pragma unroll
-                    for (int e = 0; e < 8; e++) o[e] = (bf16)v[e];
-                    const uint32_t off = j < N ? (uint32_t)((r * ldo + j) * 2) : 0x80000000u;
-                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), rs_out, off,
-                                                           0, ST_NT);
-                    if (EPI == EPI_BF16_GELU) {
-                        bf16x8 ga;
+                        for (int e = 0; e < 8; e++) o[e] = (bf16)v[e];
+                        const uint32_t off =
+                            j < N ? (uint32_t)(((fm * 32 + r) * ldo + j) * 2) : 0x80000000u;
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), rs_out,
+                                                               off, 0, ST_NT);
+                        if constexpr (EPI == EPI_BF16_GELU) {
+                            bf16x8 ga;
 #pragma unroll
-                        for (int e = 0; e < 8; e++) ga[e] = (bf16)gelu_fast((float)o[e]);
-                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ga),
-                                                               rs_out2, off, 0, ST_NT);
+                            for (int e = 0; e < 8; e++) ga[e] = (bf16)gelu_fast((float)o[e]);
+                            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ga),
+                                                                   rs_out2, off, 0, ST_NT);
+                        }
                     }
                 }
             }
+            epi_after = issued;
+            c_it += G;
+            if (c_it >= total) break;
+            decode(tile_at(c_it), c_q, c_tm, c_tn);
+            c_kt = 0;
+            c_nk = g.p[c_q].K / BK;
+#pragma unroll
+            for (int a2 = 0; a2 < FN; a2++)
+#pragma unroll
+                for (int b2 = 0; b2 < FM; b2++) acc[a2][b2] = floatx16{};
         }
-        if (!has_next) break;
-        it = it_next;
-        qc = qn;
-        tm = tm_n;
-        tn = tn_n;
-        first = false;
+        step++;
+        slot_c = slot_c + 1 == S ? 0 : slot_c + 1;
+        slot_l = slot_l + 1 == S ? 0 : slot_l + 1;
     }
-    (void)S;
 #endif
 }
 
-// Launch helper for one tile shape: the grid is min(total tiles, two blocks
-// per CU).
-template <int BM, int BN, int BK, int WM, int WN, int GM>
+// Launch helper for one tile shape: the grid is min(total tiles, OCC blocks
+// per CU on 256 CUs).
+template <int BM, int BN, int BK, int WM, int WN, int GM, int S, int OCC>
 struct GemmLds {
-    static constexpr int bm = BM, bn = BN, bk = BK;
-    static constexpr size_t lds_bytes = (size_t)2 * (BM + BN) * BK * sizeof(bf16);
+    static constexpr int bm = BM, bn = BN, bk = BK, slots = OCC * 256;
+    static constexpr size_t lds_bytes = (size_t)S * (BM + BN) * BK * sizeof(bf16);
 
     static int tiles(int M, int N) { return ceil_div(M, BM) * ceil_div(N, BN); }
 
     template <bool XRC, bool YRC, int EPI>
     static void run(const GemmGroup& g, hipStream_t st) {
         const int total = g.first_tile[g.count];
-        const int grid = total < 2 * 256 ? total : 2 * 256;
-        gemm_persistent_kernel<BM, BN, BK, WM, WN, GM, XRC, YRC, EPI>
+        const int grid = total < slots ? total : slots;
+        gemm_stream_kernel<BM, BN, BK, WM, WN, GM, S, OCC, XRC, YRC, EPI>
             <<<grid, WM * WN * 64, lds_bytes, st>>>(g);
     }
 
@@ -525,7 +584,7 @@ struct GemmLds {
     template <bool XRC, bool YRC, int EPI>
     static hipError_t prepare() {
         return hipFuncSetAttribute(
-            (const void*)gemm_persistent_kernel<BM, BN, BK, WM, WN, GM, XRC, YRC, EPI>,
+            (const void*)gemm_stream_kernel<BM, BN, BK, WM, WN, GM, S, OCC, XRC, YRC, EPI>,
             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
     }
 };

@@ -3,7 +3,7 @@
 //   backward dx = dy W       X = dy (p-contig), Y = W  (row-contig)
 //   backward dW = dy^T x     X = dy (row-contig), Y = x (row-contig)
 // Shapes whose reduction length is a multiple of 64 run on the persistent
-// direct-to-LDS kernel (gemm_lds.h); others on the register-staged kernel
+// streaming direct-to-LDS kernel (gemm_lds.h); others on the register-staged kernel
 // (gemm_mfma.h). A single weight gradient with few output tiles is split along
 // its B*T reduction (one problem of the group per split), each split writing
 // an fp32 partial that a second kernel sums in split order (deterministic);
@@ -25,12 +25,13 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(float* __restrict__ o
 
 // 128x192 tiles on four waves (64x96 each) with an 80 KB two-stage ring: two
 // blocks share a CU, so one block's barrier and load waits overlap the other's
-// matrix products. 16384-row outputs of width 768, 2304 and 3072 make exactly
-// 1, 3 and 4 rounds of 512 tiles.
+// matrix products (measured: deeper rings of 32-deep stages, and 256-row tiles
+// at one block per CU, are slower). 16384-row outputs of width 768, 2304 and
+// 3072 make exactly 1, 3 and 4 rounds of 512 tiles.
 using Cfg = GemmCfg<128, 128, 32, 2, 2, 16>;  // register-staged fallback
-using Lds = GemmLds<128, 192, 64, 2, 2, 8>;
+using Lds = GemmLds<128, 192, 64, 2, 2, 8, 2, 2>;
 constexpr int LDS_BK = 64;
-constexpr int BLOCK_SLOTS = 2 * 256;  // resident blocks: two per CU on 256 CUs
+constexpr int BLOCK_SLOTS = Lds::slots;  // resident blocks: two per CU on 256 CUs
 
 // The direct-to-LDS kernels use more than 64 KB of LDS; raise their limits once.
 static void prepare_lds_kernels() {
