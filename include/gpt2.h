@@ -131,15 +131,48 @@ int gpt2_backward(gpt2* h);
 int gpt2_update(gpt2* h, float lr, float beta1, float beta2, float eps, float weight_decay,
                 int32_t step);
 
+/* Learning-rate schedule and gradient clipping for gpt2_update_scheduled
+ * (page "Building GPT-2 from scratch", exercise table row A5 names LR
+ * schedules and gradient clipping as the training step's infrastructure).
+ * For AdamW step t >= 1:
+ *   t <= warmup_steps:  lr = lr_max * t / warmup_steps          (linear warmup)
+ *   otherwise:          p  = min(1, (t - warmup_steps) / (total_steps - warmup_steps)),
+ *                       lr = lr_min + (lr_max - lr_min) (1 + cos(pi p)) / 2  (cosine decay)
+ * Clipping (grad_clip > 0): with ||g|| = sqrt(sum of the squares of all N
+ * gradient elements), g is used as g * grad_clip / ||g|| when ||g|| >
+ * grad_clip, unchanged otherwise; grad_clip <= 0 turns it off. Requires
+ * 0 <= warmup_steps < total_steps. */
+typedef struct gpt2_schedule {
+    float lr_max;          /* peak learning rate, reached at t = warmup_steps  */
+    float lr_min;          /* learning rate from t = total_steps on            */
+    int32_t warmup_steps;  /* linear warmup steps (0: start at lr_max)         */
+    int32_t total_steps;   /* end of the cosine decay                          */
+    float beta1, beta2, eps, weight_decay; /* AdamW constants (gpt2_update)   */
+    float grad_clip;       /* global L2-norm threshold; <= 0: no clipping      */
+} gpt2_schedule;
+
+/* The schedule's learning rate at AdamW step `step` (host only, no device
+ * work); -1 if s is NULL, step < 1 or the schedule is invalid. */
+float gpt2_schedule_lr(const gpt2_schedule* s, int32_t step);
+
+/* gpt2_update with the learning rate of s at `step` and, if s->grad_clip > 0,
+ * the gradient clipped to that global L2 norm first. The norm is computed on
+ * the device in a fixed order (deterministic) and left in the activation
+ * "grad_norm" (one fp32); nothing is read back to the host. The gradient
+ * region itself is not modified. */
+int gpt2_update_scheduled(gpt2* h, const gpt2_schedule* s, int32_t step);
+
 /* Device pointer to a parameter-buffer region (GPT2_REGION_*). */
 int gpt2_region(gpt2* h, int which, void** d_ptr);
 
 /* Device pointer and size in bytes of a named activation, for inspection:
  * "encoded", "ln1", "ln1_mean", "ln1_rstd", "qkv", "atty", "att_lse",
  * "residual2", "ln2", "ln2_mean", "ln2_rstd", "fch", "fch_gelu", "residual3",
- * "lnf", "lnf_mean", "lnf_rstd", "logits", "losses", "loss". Per-layer
+ * "lnf", "lnf_mean", "lnf_rstd", "logits", "losses", "loss", "grad_norm" (the
+ * norm of the last clipped gpt2_update_scheduled). Per-layer
  * activations are stacked (L, ...). Element type: fp32 for the statistics,
- * "att_lse", "losses" and "loss"; the mode's activation type otherwise. */
+ * "att_lse", "losses", "loss" and "grad_norm"; the mode's activation type
+ * otherwise. */
 int gpt2_act(gpt2* h, const char* name, void** d_ptr, int64_t* bytes);
 
 /* Kernel timing, for measuring each kernel against its roofline. After

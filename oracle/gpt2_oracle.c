@@ -368,18 +368,48 @@ void oracle_crossentropy_softmax_backward(real* dlogits, const real* probs,
 /* AdamW, step t >= 1, decoupled weight decay scaled by lr:
  * m = b1 m + (1-b1) g; v = b2 v + (1-b2) g^2; mhat = m/(1-b1^t); vhat = v/(1-b2^t);
  * theta -= lr (mhat / (sqrt(vhat) + eps) + wd theta). */
-void oracle_adamw(real* theta, const real* g, real* m, real* v, int64_t N, real lr,
-                  real b1, real b2, real eps, real wd, int t) {
+/* The same step with every gradient element multiplied by gscale first (the
+ * gradient-clipping factor below; gscale = 1 is the plain step). */
+void oracle_adamw_scaled(real* theta, const real* g, real* m, real* v, int64_t N, real lr,
+                         real b1, real b2, real eps, real wd, int t, real gscale) {
     real c1 = 1 - pow(b1, t);
     real c2 = 1 - pow(b2, t);
 #pragma omp parallel for
     for (int64_t i = 0; i < N; i++) {
-        m[i] = b1 * m[i] + (1 - b1) * g[i];
-        v[i] = b2 * v[i] + (1 - b2) * g[i] * g[i];
+        real gi = g[i] * gscale;
+        m[i] = b1 * m[i] + (1 - b1) * gi;
+        v[i] = b2 * v[i] + (1 - b2) * gi * gi;
         real mhat = m[i] / c1;
         real vhat = v[i] / c2;
         theta[i] -= lr * (mhat / (sqrt(vhat) + eps) + wd * theta[i]);
     }
+}
+
+void oracle_adamw(real* theta, const real* g, real* m, real* v, int64_t N, real lr,
+                  real b1, real b2, real eps, real wd, int t) {
+    oracle_adamw_scaled(theta, g, m, v, N, lr, b1, b2, eps, wd, t, 1);
+}
+
+/* Training infrastructure of page "Building GPT-2 from scratch", exercise
+ * table row A5 ("LR schedules, grad clipping"). The page names them only;
+ * these are the plain readings.
+ *
+ * Global gradient norm: the Euclidean norm of the whole flat gradient,
+ * sqrt(sum_i g_i^2), summed in index order. */
+real oracle_grad_norm(const real* g, int64_t N) {
+    real s = 0;
+    for (int64_t i = 0; i < N; i++) s += g[i] * g[i];
+    return sqrt(s);
+}
+
+/* Learning rate at AdamW step t >= 1: linear warmup to lr_max over the first
+ * `warmup` steps, then a half cosine from lr_max (at t = warmup) down to
+ * lr_min (at t = total), lr_min after that. */
+double oracle_lr_schedule(double lr_max, double lr_min, int warmup, int total, int t) {
+    if (t <= warmup) return lr_max * t / warmup;
+    double p = (double)(t - warmup) / (double)(total - warmup);
+    if (p > 1) p = 1;
+    return lr_min + 0.5 * (lr_max - lr_min) * (1 + cos(ORACLE_PI * p));
 }
 
 /* ------------------------------------------------------------------------ */
@@ -657,6 +687,23 @@ void oracle_update(oracle_model* M, double lr, double b1, double b2, double eps,
                    int t) {
     oracle_adamw(M->params, M->grads, M->m, M->v, M->n_params, (real)lr, (real)b1, (real)b2,
                  (real)eps, (real)wd, t);
+}
+
+/* AdamW step t at the scheduled learning rate; with grad_clip > 0 the
+ * gradient is scaled by grad_clip / ||g|| when its global norm exceeds
+ * grad_clip. Returns ||g|| (0 when clipping is off). */
+double oracle_update_scheduled(oracle_model* M, double lr_max, double lr_min, int warmup,
+                               int total, double b1, double b2, double eps, double wd,
+                               double grad_clip, int t) {
+    double lr = oracle_lr_schedule(lr_max, lr_min, warmup, total, t);
+    real scale = 1, norm = 0;
+    if (grad_clip > 0) {
+        norm = oracle_grad_norm(M->grads, M->n_params);
+        if (norm > grad_clip) scale = (real)grad_clip / norm;
+    }
+    oracle_adamw_scaled(M->params, M->grads, M->m, M->v, M->n_params, (real)lr, (real)b1,
+                        (real)b2, (real)eps, (real)wd, t, scale);
+    return (double)norm;
 }
 
 /* ------------------------------------------------------------------------ */

@@ -85,6 +85,15 @@ def load(precision="f64"):
                                                         ct.c_int]),
         "oracle_adamw": (None, [R, R, R, R, ct.c_int64, real, real, real, real, real,
                                 ct.c_int]),
+        "oracle_adamw_scaled": (None, [R, R, R, R, ct.c_int64, real, real, real, real, real,
+                                       ct.c_int, real]),
+        "oracle_grad_norm": (real, [R, ct.c_int64]),
+        "oracle_lr_schedule": (ct.c_double, [ct.c_double, ct.c_double, ct.c_int, ct.c_int,
+                                             ct.c_int]),
+        "oracle_update_scheduled": (ct.c_double, [P, ct.c_double, ct.c_double, ct.c_int,
+                                                  ct.c_int, ct.c_double, ct.c_double,
+                                                  ct.c_double, ct.c_double, ct.c_double,
+                                                  ct.c_int]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -153,6 +162,13 @@ class Oracle:
 
     def update(self, lr, beta1, beta2, eps, wd, t):
         self.lib.oracle_update(self.h, lr, beta1, beta2, eps, wd, int(t))
+
+    def update_scheduled(self, lr_max, lr_min, warmup, total, beta1, beta2, eps, wd, grad_clip,
+                         t):
+        """Scheduled (and, with grad_clip > 0, clipped) AdamW step; returns
+        the global gradient norm (0 without clipping)."""
+        return self.lib.oracle_update_scheduled(self.h, lr_max, lr_min, int(warmup), int(total),
+                                                beta1, beta2, eps, wd, grad_clip, int(t))
 
     def _get(self, fn):
         out = np.empty(self.n, np.float64)

@@ -43,13 +43,15 @@ def cosine(a, b):
     return float(np.dot(a, b) / (na * nb))
 
 
-def gpu_steps(w, params, toks, steps, keep_grads_at=(1,), want=("params", "m", "v")):
+def gpu_steps(w, params, toks, steps, keep_grads_at=(1,), want=("params", "m", "v"), sched=None):
     """Runs `steps` training steps through the C ABI; returns per-step losses,
-    the gradients after the listed steps (fp64 numpy) and the final regions."""
+    the gradients after the listed steps (fp64 numpy) and the final regions.
+    sched (dict: lr_max, lr_min, warmup, total, grad_clip) switches to the
+    scheduled, clipped update and records the gradient norm of each step."""
     import torch
     from transformer_lm_amd import gpt2
     model = gpt2.GPT2(gpt2.config(w), params)
-    out = {"losses": [], "grads": {}}
+    out = {"losses": [], "grads": {}, "norms": []}
     for s in range(steps):
         x, y = synth.split_batch(toks[s])
         xd = torch.from_numpy(x).cuda()
@@ -58,7 +60,11 @@ def gpu_steps(w, params, toks, steps, keep_grads_at=(1,), want=("params", "m", "
         model.backward()
         if s + 1 in keep_grads_at:
             out["grads"][s + 1] = model.region(gpt2.REGION_GRAD).double().cpu().numpy()
-        model.update(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, s + 1)
+        if sched is None:
+            model.update(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, s + 1)
+        else:
+            model.update_scheduled(schedule_struct(w, sched), s + 1)
+            out["norms"].append(float(model.act("grad_norm")[0].item()))
     torch.cuda.synchronize()
     if "params" in want:
         out["params"] = model.region(gpt2.REGION_MASTER).double().cpu().numpy()
@@ -70,17 +76,29 @@ def gpu_steps(w, params, toks, steps, keep_grads_at=(1,), want=("params", "m", "
     return out
 
 
-def oracle_steps(w, params, toks, steps, keep_grads_at=(1,), precision="f64", threads=None):
+def schedule_struct(w, sched):
+    from transformer_lm_amd import gpt2
+    return gpt2.Schedule(sched["lr_max"], sched["lr_min"], sched["warmup"], sched["total"],
+                         w.beta1, w.beta2, w.eps, w.weight_decay, sched["grad_clip"])
+
+
+def oracle_steps(w, params, toks, steps, keep_grads_at=(1,), precision="f64", threads=None,
+                 sched=None):
     from oracle.wrapper import Oracle
     o = Oracle(w, params, precision=precision, threads=threads)
-    out = {"losses": [], "grads": {}}
+    out = {"losses": [], "grads": {}, "norms": []}
     for s in range(steps):
         x, y = synth.split_batch(toks[s])
         out["losses"].append(o.forward(x, y))
         o.backward()
         if s + 1 in keep_grads_at:
             out["grads"][s + 1] = o.grads()
-        o.update(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, s + 1)
+        if sched is None:
+            o.update(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, s + 1)
+        else:
+            out["norms"].append(o.update_scheduled(
+                sched["lr_max"], sched["lr_min"], sched["warmup"], sched["total"], w.beta1,
+                w.beta2, w.eps, w.weight_decay, sched["grad_clip"], s + 1))
     out["params"] = o.params()
     out["m"] = o.m()
     out["v"] = o.v()

@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(g):
     names = declared_functions()
-    assert len(names) == 16
+    assert len(names) == 18
     lib = ct.CDLL(g.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -88,4 +88,8 @@ def test_null_handle_calls_fail_cleanly(g):
     assert g._lib.gpt2_backward(None) == g.GPT2_EINVAL
     assert g._lib.gpt2_update(None, 1e-3, 0.9, 0.999, 1e-8, 0.0, 1) == g.GPT2_EINVAL
     assert g._lib.gpt2_forward(None, None, None, None) == g.GPT2_EINVAL
+    s = g.Schedule(6e-4, 6e-5, 10, 100, 0.9, 0.95, 1e-8, 0.1, 1.0)
+    assert g._lib.gpt2_update_scheduled(None, ct.byref(s), 1) == g.GPT2_EINVAL
+    assert g._lib.gpt2_schedule_lr(None, 1) == -1.0
+    assert g._lib.gpt2_schedule_lr(ct.byref(s), 0) == -1.0
     g._lib.gpt2_free(None)

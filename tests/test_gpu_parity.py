@@ -92,6 +92,47 @@ def test_fp32_step_matches_oracle(name):
     assert dth[~small].max() <= 1e-4 * w.lr + 1e-6 * np.abs(ref["params"]).max()
 
 
+@pytest.mark.parametrize("name", ["tiny", "gpt2_124m_fp32"])
+def test_fp32_scheduled_clipped_step_matches_oracle(name):
+    """The scheduled update with gradient clipping active: warmup puts the
+    first step at lr_max / 4; the threshold is a tenth of the gradient norm,
+    so m and v carry the clipped gradient; the device norm matches the
+    oracle's."""
+    from oracle.wrapper import Oracle
+    w = WORKLOADS[name]
+    p, toks = _inputs(w)
+    x, y = synth.split_batch(toks[0])
+    o = Oracle(w, p)
+    o.forward(x, y)
+    o.backward()
+    norm = float(np.linalg.norm(o.grads()))
+    sched = {"lr_max": 4 * w.lr, "lr_min": 0.1 * w.lr, "warmup": 4, "total": 20,
+             "grad_clip": 0.1 * norm}
+    lr = w.lr  # 4 lr * 1 / 4 at step 1
+    say(f"fp32 scheduled step {name}: |g| = {norm:.4e}, clip {sched['grad_clip']:.4e}")
+    gpu = gpu_steps(w, p, toks, 1, sched=sched)
+    ref = oracle_steps(w, p, toks, 1, sched=sched)
+    check_fp32(w, gpu, ref)
+    assert abs(gpu["norms"][0] - ref["norms"][0]) <= 1e-4 * ref["norms"][0]
+    assert abs(ref["norms"][0] - norm) <= 1e-12 * norm
+    assert rel_err(gpu["m"], ref["m"]) <= 1e-3
+    assert rel_err(gpu["v"], ref["v"]) <= 2e-3
+    # m holds (1 - b1) times the clipped gradient: its norm is (1 - b1) * clip
+    assert abs(np.linalg.norm(gpu["m"]) - (1 - w.beta1) * sched["grad_clip"]) <= \
+        1e-4 * sched["grad_clip"]
+    # theta: the step is lr * g' / (|g'| + eps) with g' the clipped gradient,
+    # ten times smaller than g, so eps weighs ten times more: elements below a
+    # hundredth of their tensor's largest gradient only need to stay within lr
+    g = ref["grads"][1]
+    dth = np.abs(gpu["params"] - ref["params"])
+    small = np.zeros_like(g, dtype=bool)
+    for n, gt in per_tensor(w, g).items():
+        off, s = param_offsets(w)[n]
+        small[off:off + gt.size] = np.abs(gt) < 1e-2 * np.abs(gt).max()
+    assert dth[small].max(initial=0) <= 2 * lr
+    assert dth[~small].max() <= 1e-4 * lr + 1e-6 * np.abs(ref["params"]).max()
+
+
 def test_fp32_step_skewed_tokens():
     """Tokens drawn almost all from a few ids: one token's positions span many
     of the summation ranges of the embedding backward (and two position

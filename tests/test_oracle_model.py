@@ -190,6 +190,34 @@ def test_multi_step_training_matches_torch_adamw(oracle_lib):
     assert np.allclose(o.params(), m.flat.detach().numpy(), rtol=0, atol=1e-12)
 
 
+def test_scheduled_clipped_training_matches_torch(oracle_lib):
+    """Three scheduled steps with the gradient clipped every step against
+    torch: clip_grad_norm_ (whose extra 1e-6 in the divisor is the only
+    difference) and AdamW at the schedule's learning rate."""
+    w, p, _, _ = _setup("tiny")
+    w = w.with_batch(steps=3)
+    toks = synth.tokens(w)
+    o = Oracle(w, p)
+    m = TorchGPT2(w, p.astype(np.float64))
+    opt = torch.optim.AdamW([m.flat], lr=1e-2, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.1)
+    lr_max, lr_min, warmup, total, clip = 1e-2, 1e-3, 2, 5, 0.05
+    for t in range(1, 4):
+        x, y = synth.split_batch(toks[t - 1])
+        o.forward(x, y)
+        o.backward()
+        norm = o.update_scheduled(lr_max, lr_min, warmup, total, 0.9, 0.999, 1e-8, 0.1, clip, t)
+        opt.zero_grad()
+        m.loss(x, y).backward()
+        tn = torch.nn.utils.clip_grad_norm_([m.flat], clip)
+        # equal at step 1; later steps see parameters that moved by torch's
+        # slightly different scale
+        assert norm == pytest.approx(float(tn), rel=1e-12 if t == 1 else 1e-7) and norm > clip
+        for grp in opt.param_groups:
+            grp["lr"] = oracle_lib.oracle_lr_schedule(lr_max, lr_min, warmup, total, t)
+        opt.step()
+    assert np.allclose(o.params(), m.flat.detach().numpy(), rtol=0, atol=1e-7)
+
+
 def test_backward_without_targets_is_an_error(oracle_lib):
     w, p, x, _ = _setup("tiny")
     o = Oracle(w, p)

@@ -362,3 +362,98 @@ def test_constants_used_by_the_oracle():
     assert "#define LN_EPS 1e-5" in src
     assert "0.044715" in src
     assert math.isclose(float(src.split("#define ORACLE_PI ")[1].split()[0]), math.pi, rel_tol=1e-16)
+
+
+# ------------------------------------------- LR schedule and gradient norm --
+# Page "Building GPT-2 from scratch", exercise table row A5, names LR schedules
+# and gradient clipping without formulas; the oracle takes the plain readings
+# (linear warmup then half-cosine decay; global L2 norm, scaled down to the
+# threshold). These pins fix special values and shapes of those readings.
+
+def test_grad_norm_pins(oracle_lib):
+    n = 1000
+    assert oracle_lib.oracle_grad_norm(ptr(_c(np.full(n, -3.0)), D), n) == pytest.approx(
+        3.0 * math.sqrt(n), rel=1e-15)
+    e = np.zeros(n)
+    e[417] = -2.5
+    assert oracle_lib.oracle_grad_norm(ptr(_c(e), D), n) == 2.5
+    assert oracle_lib.oracle_grad_norm(ptr(_c(np.zeros(n)), D), n) == 0.0
+    g = _c(_rng(21).normal(size=12345))
+    assert oracle_lib.oracle_grad_norm(ptr(g, D), g.size) == pytest.approx(
+        np.linalg.norm(g), rel=1e-13)
+
+
+def test_scaled_adamw_carries_the_scaled_gradient(oracle_lib):
+    """With beta1 = 0 the first moment is the (scaled) gradient itself; with
+    scale 1 the step equals the plain AdamW step bit for bit."""
+    r = _rng(22)
+    n = 50
+    th0, g = _c(r.normal(size=n)), _c(r.normal(size=n))
+    th, m, v = th0.copy(), np.zeros(n), np.zeros(n)
+    oracle_lib.oracle_adamw_scaled(ptr(th, D), ptr(g, D), ptr(m, D), ptr(v, D), n, 1e-3, 0.0,
+                                   0.999, 1e-8, 0.0, 1, 0.25)
+    assert np.array_equal(m, 0.25 * g)
+    assert np.allclose(v, 0.001 * (0.25 * g) ** 2, rtol=1e-14)
+    th1, m1, v1 = th0.copy(), np.zeros(n), np.zeros(n)
+    th2, m2, v2 = th0.copy(), np.zeros(n), np.zeros(n)
+    oracle_lib.oracle_adamw_scaled(ptr(th1, D), ptr(g, D), ptr(m1, D), ptr(v1, D), n, 1e-3, 0.9,
+                                   0.999, 1e-8, 0.1, 3, 1.0)
+    _adamw(oracle_lib, th2, g, m2, v2, 1e-3, 0.9, 0.999, 1e-8, 0.1, 3)
+    assert np.array_equal(th1, th2) and np.array_equal(m1, m2) and np.array_equal(v1, v2)
+
+
+def test_clipping_matches_torch_clip_grad_norm(oracle_lib):
+    """torch.nn.utils.clip_grad_norm_ scales by max_norm / (norm + 1e-6), capped at
+    1; the oracle's reading has no 1e-6, so the two agree to ~1e-6 relative."""
+    r = _rng(23)
+    n = 300
+    th0 = _c(r.normal(size=n))
+    g = _c(r.normal(size=n) * 3)
+    for max_norm in (0.5, 1e6):
+        norm = oracle_lib.oracle_grad_norm(ptr(g, D), n)
+        scale = max_norm / norm if norm > max_norm else 1.0
+        th, m, v = th0.copy(), np.zeros(n), np.zeros(n)
+        oracle_lib.oracle_adamw_scaled(ptr(th, D), ptr(g, D), ptr(m, D), ptr(v, D), n, 1e-3, 0.9,
+                                       0.999, 1e-8, 0.1, 1, scale)
+        p = torch.nn.Parameter(torch.from_numpy(th0.copy()))
+        p.grad = torch.from_numpy(g.copy())
+        tn = torch.nn.utils.clip_grad_norm_([p], max_norm)
+        assert float(tn) == pytest.approx(norm, rel=1e-13)
+        assert np.allclose(m, 0.1 * p.grad.numpy(), rtol=2e-6, atol=0)
+
+
+def _lr(lib, t, lr_max=6e-4, lr_min=6e-5, warmup=100, total=1100):
+    return lib.oracle_lr_schedule(lr_max, lr_min, warmup, total, t)
+
+
+def test_lr_schedule_special_points(oracle_lib):
+    lib = oracle_lib
+    # linear warmup: lr_max / warmup at t = 1, half at t = warmup / 2, lr_max at warmup
+    assert _lr(lib, 1) == pytest.approx(6e-6, rel=1e-15)
+    assert _lr(lib, 50) == pytest.approx(3e-4, rel=1e-15)
+    assert _lr(lib, 100) == pytest.approx(6e-4, rel=1e-15)
+    # cosine: midpoint halfway between lr_max and lr_min, end and beyond at lr_min
+    assert _lr(lib, 600) == pytest.approx(3.3e-4, rel=1e-14)
+    assert _lr(lib, 1100) == pytest.approx(6e-5, rel=1e-14)
+    assert _lr(lib, 5000) == pytest.approx(6e-5, rel=1e-14)
+    # symmetric about the midpoint, non-increasing, and flat where it starts
+    # (second order in the progress p: a linear decay would drop 1e-3 here)
+    lrs = [_lr(lib, t) for t in range(100, 1101)]
+    assert all(a >= b for a, b in zip(lrs, lrs[1:]))
+    for k in (1, 137, 400):
+        assert _lr(lib, 100 + k) + _lr(lib, 1100 - k) == pytest.approx(6.6e-4, rel=1e-13)
+    drop = (6e-4 - _lr(lib, 101)) / (6e-4 - 6e-5)
+    assert drop == pytest.approx((math.pi * 1e-3) ** 2 / 4, rel=1e-3)
+    # no warmup: the cosine starts at step 0, so step 5 of 10 is the midpoint
+    assert lib.oracle_lr_schedule(1e-3, 0.0, 0, 10, 5) == pytest.approx(5e-4, rel=1e-14)
+    assert lib.oracle_lr_schedule(1e-3, 0.0, 0, 10, 10) == pytest.approx(0.0, abs=1e-20)
+
+
+def test_library_schedule_matches_the_oracle(oracle_lib):
+    """gpt2_schedule_lr (host code of the library) against the oracle."""
+    from transformer_lm_amd import gpt2
+    s = gpt2.Schedule(6e-4, 6e-5, 100, 1100, 0.9, 0.95, 1e-8, 0.1, 1.0)
+    for t in (1, 2, 37, 99, 100, 101, 350, 600, 1099, 1100, 1500):
+        assert gpt2.schedule_lr(s, t) == pytest.approx(_lr(oracle_lib, t), rel=2e-7, abs=1e-12)
+    with pytest.raises(gpt2.GPT2Error):
+        gpt2.schedule_lr(gpt2.Schedule(6e-4, 6e-5, 10, 10, 0.9, 0.95, 1e-8, 0.1, 1.0), 1)

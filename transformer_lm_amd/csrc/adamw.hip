@@ -24,19 +24,29 @@ __device__ __forceinline__ void st_nt(float* p, f32x4 x) {
     __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(p));
 }
 
+// Gradient clipping factor: clip / ||g|| when the norm (device scalar, from
+// grad_norm) exceeds clip, else 1 (also without a norm).
+__device__ __forceinline__ float clip_scale(const float* gnorm, float clip) {
+    if (!gnorm) return 1.f;
+    const float nrm = *gnorm;
+    return nrm > clip ? clip / nrm : 1.f;
+}
+
 __global__ __launch_bounds__(256) void adamw_kernel(float* __restrict__ theta,
                                                     const float* __restrict__ g,
                                                     float* __restrict__ m, float* __restrict__ v,
                                                     bf16* __restrict__ theta_bf16, int64_t n,
                                                     float lr, float b1, float b2, float eps,
-                                                    float wd, float c1, float c2) {
+                                                    float wd, float c1, float c2,
+                                                    const float* __restrict__ gnorm, float clip) {
     typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    const float gs = clip_scale(gnorm, clip);
     const int64_t n8 = n / 8;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n8; i += stride) {
         const int64_t e0 = i * 4, e1 = (i + n8) * 4;  // two groups n/2 apart: both streams coalesce
         f32x4 th[2] = {ld_nt(theta + e0), ld_nt(theta + e1)};
-        const f32x4 gg[2] = {ld_nt(g + e0), ld_nt(g + e1)};
+        const f32x4 gg[2] = {ld_nt(g + e0) * gs, ld_nt(g + e1) * gs};
         f32x4 mm[2] = {ld_nt(m + e0), ld_nt(m + e1)};
         f32x4 vv[2] = {ld_nt(v + e0), ld_nt(v + e1)};
 #pragma unroll
@@ -65,7 +75,7 @@ __global__ __launch_bounds__(256) void adamw_kernel(float* __restrict__ theta,
     // tail (n % 8 elements)
     for (int64_t i = n8 * 8 + blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += stride) {
         float th = theta[i], mm = m[i], vv = v[i];
-        adamw_one(th, g[i], mm, vv, lr, b1, b2, eps, wd, c1, c2);
+        adamw_one(th, g[i] * gs, mm, vv, lr, b1, b2, eps, wd, c1, c2);
         theta[i] = th;
         m[i] = mm;
         v[i] = vv;
@@ -75,10 +85,50 @@ __global__ __launch_bounds__(256) void adamw_kernel(float* __restrict__ theta,
 
 void adamw(float* theta, const float* g, float* m, float* v, bf16* theta_bf16, int64_t n,
            float lr, float b1, float b2, float eps, float wd, float c1, float c2,
-           hipStream_t st) {
+           const float* gnorm, float clip, hipStream_t st) {
     int64_t blocks = (n / 8 + 255) / 256;
     if (blocks > 8192) blocks = 8192;
     if (blocks < 1) blocks = 1;
     adamw_kernel<<<(int)blocks, 256, 0, st>>>(theta, g, m, v, theta_bf16, n, lr, b1, b2, eps, wd,
-                                              c1, c2);
+                                              c1, c2, gnorm, clip);
+}
+
+// ---------------------------------------------------------------------------
+// Global L2 norm of the gradient, the quantity that gradient clipping (page
+// "Building GPT-2 from scratch", exercise table row A5) compares against its
+// threshold: ||g|| = sqrt(sum_i g_i^2) over the whole flat array. Two fixed-
+// shape passes keep it deterministic: GNORM_BLOCKS blocks each sum the squares
+// of a fixed set of 4-float groups (thread order, then the block reduction),
+// then one block adds the partials in block order.
+#define GNORM_BLOCKS 1024
+
+int64_t grad_norm_workspace_floats() { return GNORM_BLOCKS; }
+
+__global__ __launch_bounds__(256) void grad_norm_partial_kernel(float* __restrict__ part,
+                                                                const float* __restrict__ g,
+                                                                int64_t n) {
+    __shared__ float red[16];
+    const int64_t n4 = n / 4;
+    const int64_t stride = (int64_t)GNORM_BLOCKS * 256;
+    float s = 0.f;
+    for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n4; i += stride) {
+        const f32x4 x = ld_nt(g + 4 * i);
+        s += x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
+    }
+    if (blockIdx.x == 0)  // tail (n % 4 elements)
+        for (int64_t i = 4 * n4 + threadIdx.x; i < n; i += 256) s += g[i] * g[i];
+    s = block_sum(s, red);
+    if (threadIdx.x == 0) part[blockIdx.x] = s;
+}
+
+__global__ __launch_bounds__(1024) void grad_norm_final_kernel(float* __restrict__ out,
+                                                               const float* __restrict__ part) {
+    __shared__ float red[16];
+    const float s = block_sum(part[threadIdx.x], red);  // GNORM_BLOCKS == blockDim.x
+    if (threadIdx.x == 0) out[0] = sqrtf(s);
+}
+
+void grad_norm(float* out, float* part, const float* g, int64_t n, hipStream_t st) {
+    grad_norm_partial_kernel<<<GNORM_BLOCKS, 256, 0, st>>>(part, g, n);
+    grad_norm_final_kernel<<<1, GNORM_BLOCKS, 0, st>>>(out, part);
 }

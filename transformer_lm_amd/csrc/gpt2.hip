@@ -43,7 +43,7 @@ enum {
     A_LN2, A_LN2_MEAN, A_LN2_RSTD, A_FCH, A_FCH_GELU, A_RESIDUAL3, A_LNF, A_LNF_MEAN,
     A_LNF_RSTD, A_LOGITS, A_LOSSES, A_LOSS, A_ERR,
     W_DRES, W_DC, W_D3C, W_D4C, W_ATT_D, W_LN_PART, W_BIAS_PART, W_ENC,
-    W_DW_SPLIT, NUM_A
+    W_DW_SPLIT, A_GNORM, W_GNORM_PART, NUM_A
 };
 
 const char* const A_NAMES[NUM_A] = {
@@ -51,7 +51,7 @@ const char* const A_NAMES[NUM_A] = {
     "ln2", "ln2_mean", "ln2_rstd", "fch", "fch_gelu", "residual3", "lnf", "lnf_mean",
     "lnf_rstd", "logits", "losses", "loss", "err",
     "dresidual", "dbuf_c", "dbuf_3c", "dbuf_4c", "att_d", "ln_partials", "bias_partials",
-    "enc_work", "dw_split"};
+    "enc_work", "dw_split", "grad_norm", "gnorm_partials"};
 
 constexpr int64_t ALIGN = 256;
 int64_t align_up(int64_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
@@ -155,6 +155,8 @@ void plan(const gpt2_config* c, Layout* lay) {
         }
     }
     a[W_DW_SPLIT] = dwf * 4;
+    a[A_GNORM] = 4;
+    a[W_GNORM_PART] = grad_norm_workspace_floats() * 4;
     int64_t o = 0;
     for (int i = 0; i < NUM_A; i++) {
         lay->aoff[i] = o;
@@ -627,9 +629,38 @@ int gpt2_update(gpt2* h, float lr, float beta1, float beta2, float eps, float we
     {
         KScope k(h, K_ADAMW, (double)h->lay.N * (h->pbf16 ? 30.0 : 28.0));
         adamw(h->master, h->grad, h->m, h->v, h->pbf16, h->lay.N, lr, beta1, beta2, eps,
-              weight_decay, c1, c2, h->st);
+              weight_decay, c1, c2, nullptr, 0.f, h->st);
     }
     return hip_status("gpt2_update");
+}
+
+float gpt2_schedule_lr(const gpt2_schedule* s, int32_t step) {
+    if (!s || step < 1 || s->warmup_steps < 0 || s->total_steps <= s->warmup_steps) return -1.f;
+    if (step <= s->warmup_steps) return s->lr_max * (float)step / (float)s->warmup_steps;
+    double p = (double)(step - s->warmup_steps) / (double)(s->total_steps - s->warmup_steps);
+    if (p > 1.0) p = 1.0;
+    const double pi = 3.14159265358979323846;
+    return (float)(s->lr_min + 0.5 * ((double)s->lr_max - s->lr_min) * (1.0 + cos(pi * p)));
+}
+
+int gpt2_update_scheduled(gpt2* h, const gpt2_schedule* s, int32_t step) {
+    if (!h || !s) return fail(GPT2_EINVAL, "handle or schedule is NULL");
+    if (step < 1) return fail(GPT2_EINVAL, "step must be >= 1");
+    if (s->warmup_steps < 0 || s->total_steps <= s->warmup_steps)
+        return fail(GPT2_EINVAL, "schedule needs 0 <= warmup_steps < total_steps");
+    const float lr = gpt2_schedule_lr(s, step);
+    const float c1 = (float)(1.0 - pow((double)s->beta1, (double)step));
+    const float c2 = (float)(1.0 - pow((double)s->beta2, (double)step));
+    const bool clip = s->grad_clip > 0.f;
+    {
+        KScope k(h, K_ADAMW, (double)h->lay.N * ((h->pbf16 ? 30.0 : 28.0) + (clip ? 4.0 : 0.0)));
+        float* nrm = static_cast<float*>(h->a[A_GNORM]);
+        if (clip)
+            grad_norm(nrm, static_cast<float*>(h->a[W_GNORM_PART]), h->grad, h->lay.N, h->st);
+        adamw(h->master, h->grad, h->m, h->v, h->pbf16, h->lay.N, lr, s->beta1, s->beta2, s->eps,
+              s->weight_decay, c1, c2, clip ? nrm : nullptr, s->grad_clip, h->st);
+    }
+    return hip_status("gpt2_update_scheduled");
 }
 
 int gpt2_region(gpt2* h, int which, void** d_ptr) {

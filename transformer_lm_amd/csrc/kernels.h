@@ -130,5 +130,11 @@ void classifier_fwd(T* logits, float* losses, const int32_t* targets, int N, int
 void loss_mean(float* out, const float* losses, int n, hipStream_t st);
 
 // ---- AdamW ------------------------------------------------------------------
+// gnorm: device scalar ||g|| (or nullptr: no clipping); g is scaled by
+// clip / ||g|| when ||g|| > clip.
 void adamw(float* theta, const float* g, float* m, float* v, bf16* theta_bf16, int64_t n,
-           float lr, float b1, float b2, float eps, float wd, float c1, float c2, hipStream_t st);
+           float lr, float b1, float b2, float eps, float wd, float c1, float c2,
+           const float* gnorm, float clip, hipStream_t st);
+// out[0] = sqrt(sum g_i^2), deterministic; part: grad_norm_workspace_floats().
+int64_t grad_norm_workspace_floats();
+void grad_norm(float* out, float* part, const float* g, int64_t n, hipStream_t st);

@@ -26,12 +26,21 @@ DTYPE_FP32, DTYPE_BF16 = 0, 1
 REGION_MASTER, REGION_GRAD, REGION_M, REGION_V, REGION_PARAM_BF16 = 0, 1, 2, 3, 4
 EXPORTS = ("gpt2_num_params", "gpt2_num_param_tensors", "gpt2_param_table",
            "gpt2_param_buffer_bytes", "gpt2_act_buffer_bytes", "gpt2_create", "gpt2_forward",
-           "gpt2_backward", "gpt2_update", "gpt2_region", "gpt2_act", "gpt2_free",
+           "gpt2_backward", "gpt2_update", "gpt2_schedule_lr", "gpt2_update_scheduled",
+           "gpt2_region", "gpt2_act", "gpt2_free",
            "gpt2_last_error", "gpt2_timing_arm", "gpt2_timing_classes", "gpt2_timing_read")
 
 
 class Config(ct.Structure):
     _fields_ = [(n, ct.c_int32) for n in ("V", "Vp", "max_T", "C", "L", "NH", "B", "T", "dtype")]
+
+
+class Schedule(ct.Structure):
+    """gpt2_schedule: warmup + cosine learning rate, AdamW constants, and the
+    global gradient-norm clipping threshold (<= 0: off)."""
+    _fields_ = [("lr_max", ct.c_float), ("lr_min", ct.c_float), ("warmup_steps", ct.c_int32),
+                ("total_steps", ct.c_int32), ("beta1", ct.c_float), ("beta2", ct.c_float),
+                ("eps", ct.c_float), ("weight_decay", ct.c_float), ("grad_clip", ct.c_float)]
 
 
 _P = ct.c_void_p
@@ -49,6 +58,8 @@ _SIG = {
     "gpt2_backward": (ct.c_int, [_P]),
     "gpt2_update": (ct.c_int, [_P, ct.c_float, ct.c_float, ct.c_float, ct.c_float, ct.c_float,
                                ct.c_int32]),
+    "gpt2_schedule_lr": (ct.c_float, [ct.POINTER(Schedule), ct.c_int32]),
+    "gpt2_update_scheduled": (ct.c_int, [_P, ct.POINTER(Schedule), ct.c_int32]),
     "gpt2_region": (ct.c_int, [_P, ct.c_int, ct.POINTER(_P)]),
     "gpt2_act": (ct.c_int, [_P, ct.c_char_p, ct.POINTER(_P), ct.POINTER(ct.c_int64)]),
     "gpt2_free": (None, [_P]),
@@ -123,7 +134,16 @@ def act_buffer_bytes(cfg):
 
 
 _F32_ACTS = {"ln1_mean", "ln1_rstd", "ln2_mean", "ln2_rstd", "lnf_mean", "lnf_rstd", "att_lse",
-             "losses", "loss", "att_d", "ln_partials", "bias_partials"}
+             "losses", "loss", "att_d", "ln_partials", "bias_partials", "grad_norm",
+             "gnorm_partials"}
+
+
+def schedule_lr(sched, step):
+    """Learning rate of the schedule at AdamW step `step` (host only)."""
+    lr = _lib.gpt2_schedule_lr(ct.byref(sched), int(step))
+    if lr < 0:
+        raise GPT2Error(GPT2_EINVAL, "invalid schedule or step")
+    return lr
 _I32_ACTS = {"err", "enc_work"}
 
 
@@ -184,6 +204,9 @@ class GPT2:
 
     def update(self, lr, beta1, beta2, eps, weight_decay, step):
         _check(_lib.gpt2_update(self.h, lr, beta1, beta2, eps, weight_decay, int(step)))
+
+    def update_scheduled(self, sched, step):
+        _check(_lib.gpt2_update_scheduled(self.h, ct.byref(sched), int(step)))
 
     # -- views ---------------------------------------------------------------
     def _view(self, buf, ptr, nbytes, dtype):
