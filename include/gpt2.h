@@ -162,6 +162,25 @@ float gpt2_schedule_lr(const gpt2_schedule* s, int32_t step);
  * region itself is not modified. */
 int gpt2_update_scheduled(gpt2* h, const gpt2_schedule* s, int32_t step);
 
+/* Checkpoints for bit-exact resume (page "Building GPT-2 from scratch",
+ * exercise table row A5). A checkpoint is a host image of the training state:
+ * a 128-byte header (magic "GPT2CKP1", version 1, the configuration, N and
+ * the caller's step), then the master parameters, m and v (N fp32 each, in
+ * region order). Loading it into a handle of the same model and precision
+ * (B and T may differ) restores those regions, re-derives the bf16 working
+ * copy, zeroes the gradients and returns the step; since every kernel is
+ * deterministic, training resumed from it continues bit for bit as the
+ * uninterrupted run would, given the same token stream. The caller owns the
+ * host buffer (pinned memory makes the copies faster); both calls
+ * synchronise the stream.
+ * gpt2_checkpoint_bytes: size of the image, -1 if cfg is invalid.
+ * gpt2_checkpoint_save:  writes the image; bytes >= gpt2_checkpoint_bytes().
+ * gpt2_checkpoint_load:  GPT2_EINVAL for a foreign or truncated image,
+ *                        GPT2_ESHAPE for another model; step may be NULL. */
+int64_t gpt2_checkpoint_bytes(const gpt2_config* cfg);
+int gpt2_checkpoint_save(gpt2* h, int64_t step, void* host_buf, int64_t bytes);
+int gpt2_checkpoint_load(gpt2* h, const void* host_buf, int64_t bytes, int64_t* step);
+
 /* Device pointer to a parameter-buffer region (GPT2_REGION_*). */
 int gpt2_region(gpt2* h, int which, void** d_ptr);
 

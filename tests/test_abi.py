@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(g):
     names = declared_functions()
-    assert len(names) == 18
+    assert len(names) == 21
     lib = ct.CDLL(g.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -60,6 +60,8 @@ def test_buffer_sizes(g):
     assert ab < 12e9                                  # well inside 288 GB of HBM
     w32 = WORKLOADS["tiny"]
     assert g.param_buffer_bytes(g.config(w32)) >= 16 * w32.num_params()
+    # checkpoint image: 128-byte header + master, m, v
+    assert g._lib.gpt2_checkpoint_bytes(ct.byref(cfg)) == 128 + 12 * n
 
 
 @pytest.mark.parametrize("field,value", [("C", 30), ("NH", 5), ("Vp", 60), ("T", 64),
@@ -92,4 +94,6 @@ def test_null_handle_calls_fail_cleanly(g):
     assert g._lib.gpt2_update_scheduled(None, ct.byref(s), 1) == g.GPT2_EINVAL
     assert g._lib.gpt2_schedule_lr(None, 1) == -1.0
     assert g._lib.gpt2_schedule_lr(ct.byref(s), 0) == -1.0
+    assert g._lib.gpt2_checkpoint_save(None, 1, None, 0) == g.GPT2_EINVAL
+    assert g._lib.gpt2_checkpoint_load(None, None, 0, None) == g.GPT2_EINVAL
     g._lib.gpt2_free(None)

@@ -285,6 +285,61 @@ def test_steps_are_deterministic():
     assert np.array_equal(a["params"], b["params"])
 
 
+@pytest.mark.parametrize("name", ["tiny", "gpt2_124m_B2T96"])
+def test_checkpoint_resume_is_bit_exact(name):
+    """Four steps straight through against two steps, a checkpoint, a fresh
+    handle (started from other parameters) restored from it, and the last two
+    steps on the same tokens: losses, parameters, moments and the bf16 copy
+    agree bit for bit."""
+    import torch
+    from transformer_lm_amd import gpt2
+    w = WORKLOADS["tiny"] if name == "tiny" else WORKLOADS["gpt2_124m"].with_batch(B=2, T=96)
+    w = w.with_batch(steps=4)
+    p, toks = _inputs(w)
+    say(f"checkpoint resume {name}")
+
+    def run(model, steps, losses):
+        for s in steps:
+            x, y = synth.split_batch(toks[s])
+            losses.append(model.forward(torch.from_numpy(x).cuda(), torch.from_numpy(y).cuda()))
+            model.backward()
+            model.update(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, s + 1)
+
+    def state(model):
+        regs = [gpt2.REGION_MASTER, gpt2.REGION_M, gpt2.REGION_V]
+        if model.bf16:
+            regs.append(gpt2.REGION_PARAM_BF16)
+        return [model.region(r).cpu().clone() for r in regs]
+
+    ref_losses, res_losses = [], []
+    a = gpt2.GPT2(gpt2.config(w), p)
+    run(a, range(4), ref_losses)
+    ref = state(a)
+    b = gpt2.GPT2(gpt2.config(w), p)
+    run(b, range(2), res_losses)
+    image = b.checkpoint(2)
+    del b
+    c = gpt2.GPT2(gpt2.config(w), synth.init_params(w) * 0.5)
+    assert c.restore(image) == 2
+    run(c, range(2, 4), res_losses)
+    assert res_losses == ref_losses
+    for x, y in zip(state(c), ref):
+        assert torch.equal(x, y)
+    # a foreign or mismatched image is refused
+    with pytest.raises(gpt2.GPT2Error) as e:
+        c.restore(image[:100])
+    assert e.value.code == gpt2.GPT2_EINVAL
+    bad = image.copy()
+    bad[0] ^= 1
+    with pytest.raises(gpt2.GPT2Error) as e:
+        c.restore(bad)
+    assert e.value.code == gpt2.GPT2_EINVAL
+    other = gpt2.GPT2(gpt2.config(WORKLOADS["tiny_pad"]), synth.init_params(WORKLOADS["tiny_pad"]))
+    with pytest.raises(gpt2.GPT2Error) as e:
+        other.restore(image)
+    assert e.value.code == gpt2.GPT2_ESHAPE
+
+
 def test_error_paths():
     import torch
     from transformer_lm_amd import gpt2

@@ -663,6 +663,87 @@ int gpt2_update_scheduled(gpt2* h, const gpt2_schedule* s, int32_t step) {
     return hip_status("gpt2_update_scheduled");
 }
 
+// ---------------------------------------------------------------------------
+// Checkpoints (page "Building GPT-2 from scratch", exercise table row A5:
+// bit-exact checkpoint resume). The training state is the master parameters
+// and both AdamW moments plus the step; the bf16 working copy is a function
+// of the master parameters and gradients are rebuilt by every backward pass.
+// Host image: a 128-byte header, then master, m and v (N fp32 each).
+namespace {
+constexpr char CKPT_MAGIC[8] = {'G', 'P', 'T', '2', 'C', 'K', 'P', '1'};
+constexpr int CKPT_HEADER = 128;
+struct CkptHeader {
+    char magic[8];
+    uint32_t version, header_bytes;
+    gpt2_config cfg;
+    int32_t pad0;
+    int64_t N, step;
+};
+static_assert(sizeof(CkptHeader) <= CKPT_HEADER, "checkpoint header");
+
+bool same_model(const gpt2_config& a, const gpt2_config& b) {
+    return a.V == b.V && a.Vp == b.Vp && a.max_T == b.max_T && a.C == b.C && a.L == b.L &&
+           a.NH == b.NH && a.dtype == b.dtype;
+}
+}  // namespace
+
+int64_t gpt2_checkpoint_bytes(const gpt2_config* cfg) {
+    const int64_t n = gpt2_num_params(cfg);
+    return n < 0 ? -1 : CKPT_HEADER + 3 * n * (int64_t)sizeof(float);
+}
+
+int gpt2_checkpoint_save(gpt2* h, int64_t step, void* host_buf, int64_t bytes) {
+    if (!h || !host_buf) return fail(GPT2_EINVAL, "handle or host_buf is NULL");
+    const int64_t need = gpt2_checkpoint_bytes(&h->cfg);
+    if (bytes < need) return fail(GPT2_EINVAL, "host_buf is smaller than gpt2_checkpoint_bytes()");
+    CkptHeader hd;
+    memset(&hd, 0, sizeof(hd));
+    memcpy(hd.magic, CKPT_MAGIC, 8);
+    hd.version = 1;
+    hd.header_bytes = CKPT_HEADER;
+    hd.cfg = h->cfg;
+    hd.N = h->lay.N;
+    hd.step = step;
+    char* out = static_cast<char*>(host_buf);
+    memset(out, 0, CKPT_HEADER);
+    memcpy(out, &hd, sizeof(hd));
+    const size_t nb = (size_t)h->lay.N * sizeof(float);
+    const float* src[3] = {h->master, h->m, h->v};
+    for (int i = 0; i < 3; i++)
+        if (hipMemcpyAsync(out + CKPT_HEADER + i * nb, src[i], nb, hipMemcpyDeviceToHost, h->st) !=
+            hipSuccess)
+            return fail(GPT2_EHIP, "gpt2_checkpoint_save: copy to the host failed");
+    if (hipStreamSynchronize(h->st) != hipSuccess)
+        return fail(GPT2_EHIP, "gpt2_checkpoint_save: stream synchronisation failed");
+    return hip_status("gpt2_checkpoint_save");
+}
+
+int gpt2_checkpoint_load(gpt2* h, const void* host_buf, int64_t bytes, int64_t* step) {
+    if (!h || !host_buf) return fail(GPT2_EINVAL, "handle or host_buf is NULL");
+    if (bytes < CKPT_HEADER) return fail(GPT2_EINVAL, "checkpoint shorter than its header");
+    CkptHeader hd;
+    memcpy(&hd, host_buf, sizeof(hd));
+    if (memcmp(hd.magic, CKPT_MAGIC, 8) != 0 || hd.version != 1 || hd.header_bytes != CKPT_HEADER)
+        return fail(GPT2_EINVAL, "not a checkpoint of this format");
+    if (!same_model(hd.cfg, h->cfg) || hd.N != h->lay.N)
+        return fail(GPT2_ESHAPE, "checkpoint of a different model or precision");
+    if (bytes < gpt2_checkpoint_bytes(&h->cfg)) return fail(GPT2_EINVAL, "checkpoint truncated");
+    const char* in = static_cast<const char*>(host_buf);
+    const size_t nb = (size_t)h->lay.N * sizeof(float);
+    float* dst[3] = {h->master, h->m, h->v};
+    for (int i = 0; i < 3; i++)
+        if (hipMemcpyAsync(dst[i], in + CKPT_HEADER + i * nb, nb, hipMemcpyHostToDevice, h->st) !=
+            hipSuccess)
+            return fail(GPT2_EHIP, "gpt2_checkpoint_load: copy to the device failed");
+    fill_zero_f32(h->grad, h->lay.N, h->st);
+    if (h->pbf16) round_to_bf16(h->pbf16, h->master, h->lay.N, h->st);
+    h->fwd_targets = false;
+    if (hipStreamSynchronize(h->st) != hipSuccess)
+        return fail(GPT2_EHIP, "gpt2_checkpoint_load: stream synchronisation failed");
+    if (step) *step = hd.step;
+    return hip_status("gpt2_checkpoint_load");
+}
+
 int gpt2_region(gpt2* h, int which, void** d_ptr) {
     if (!h || !d_ptr) return fail(GPT2_EINVAL, "handle or d_ptr is NULL");
     if (which < 0 || which > 4) return fail(GPT2_EINVAL, "unknown region");

@@ -27,6 +27,7 @@ REGION_MASTER, REGION_GRAD, REGION_M, REGION_V, REGION_PARAM_BF16 = 0, 1, 2, 3, 
 EXPORTS = ("gpt2_num_params", "gpt2_num_param_tensors", "gpt2_param_table",
            "gpt2_param_buffer_bytes", "gpt2_act_buffer_bytes", "gpt2_create", "gpt2_forward",
            "gpt2_backward", "gpt2_update", "gpt2_schedule_lr", "gpt2_update_scheduled",
+           "gpt2_checkpoint_bytes", "gpt2_checkpoint_save", "gpt2_checkpoint_load",
            "gpt2_region", "gpt2_act", "gpt2_free",
            "gpt2_last_error", "gpt2_timing_arm", "gpt2_timing_classes", "gpt2_timing_read")
 
@@ -60,6 +61,9 @@ _SIG = {
                                ct.c_int32]),
     "gpt2_schedule_lr": (ct.c_float, [ct.POINTER(Schedule), ct.c_int32]),
     "gpt2_update_scheduled": (ct.c_int, [_P, ct.POINTER(Schedule), ct.c_int32]),
+    "gpt2_checkpoint_bytes": (ct.c_int64, [_CP]),
+    "gpt2_checkpoint_save": (ct.c_int, [_P, ct.c_int64, _P, ct.c_int64]),
+    "gpt2_checkpoint_load": (ct.c_int, [_P, _P, ct.c_int64, ct.POINTER(ct.c_int64)]),
     "gpt2_region": (ct.c_int, [_P, ct.c_int, ct.POINTER(_P)]),
     "gpt2_act": (ct.c_int, [_P, ct.c_char_p, ct.POINTER(_P), ct.POINTER(ct.c_int64)]),
     "gpt2_free": (None, [_P]),
@@ -207,6 +211,20 @@ class GPT2:
 
     def update_scheduled(self, sched, step):
         _check(_lib.gpt2_update_scheduled(self.h, ct.byref(sched), int(step)))
+
+    def checkpoint(self, step):
+        """Host image of the training state (numpy uint8) at `step`."""
+        n = _lib.gpt2_checkpoint_bytes(ct.byref(self.cfg))
+        buf = np.empty(n, np.uint8)
+        _check(_lib.gpt2_checkpoint_save(self.h, int(step), buf.ctypes.data, n))
+        return buf
+
+    def restore(self, image):
+        """Loads a checkpoint image; returns its step."""
+        image = np.ascontiguousarray(image, dtype=np.uint8)
+        step = ct.c_int64()
+        _check(_lib.gpt2_checkpoint_load(self.h, image.ctypes.data, image.size, ct.byref(step)))
+        return step.value
 
     # -- views ---------------------------------------------------------------
     def _view(self, buf, ptr, nbytes, dtype):
