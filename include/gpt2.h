@@ -57,7 +57,7 @@ typedef struct gpt2_config {
                     /* a multiple of 64, >= V                                 */
     int32_t max_T;  /* rows of wpe                                            */
     int32_t C;      /* channels: a multiple of 8, at most 2048                */
-    int32_t L;      /* layers                                                 */
+    int32_t L;      /* layers, 1 .. 63                                        */
     int32_t NH;     /* heads: C % NH == 0, head size C/NH a multiple of 8,    */
                     /* at most 128                                            */
     int32_t B;      /* batch rows per step                                    */

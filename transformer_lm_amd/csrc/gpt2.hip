@@ -73,7 +73,7 @@ const char* check_config(const gpt2_config* c) {
     if (c->NH <= 0 || c->C % c->NH != 0) return "need C % NH == 0";
     int hs = c->C / c->NH;
     if (hs % 8 != 0 || hs > 128) return "need head size C/NH a multiple of 8, at most 128";
-    if (c->L <= 0) return "need L > 0";
+    if (c->L <= 0 || 2 * c->L + 1 > LN_RED_MAX) return "need 0 < L <= 63";
     if (c->max_T <= 0 || c->T <= 0 || c->T > c->max_T) return "need 1 <= T <= max_T";
     if (c->B <= 0) return "need B > 0";
     if ((int64_t)c->B * c->T > 524288) return "need B*T <= 524288";
@@ -142,7 +142,7 @@ void plan(const gpt2_config* c, Layout* lay) {
     a[W_D3C] = L * BT * 3 * C * es;
     a[W_D4C] = L * BT * 4 * C * es;
     a[W_ATT_D] = 2 * B * NH * T * 4;  // D, then the base-2 log-sum-exp
-    a[W_LN_PART] = layernorm_bwd_partials((int)C) * 4;
+    a[W_LN_PART] = layernorm_bwd_partials((int)C, (int)(2 * L + 1)) * 4;
     a[W_BIAS_PART] = bias_bwd_partials((int)BT, (int)(4 * C)) * 4;
     a[W_ENC] = encoder_bwd_workspace_bytes((int)BT, (int)V, (int)C);
     // split-reduction partials of the bf16 weight-gradient products
@@ -400,10 +400,16 @@ void backward_impl(gpt2* h) {
         KScope k(h, K_MATMUL_BWD_DW, mm_flops(Vp, C, BT));
         matmul_bwd_dw<T>(G[P_WTE], nullptr, dlogits, lnf, BT, Vp, C, dws, bp, st);
     }
+    // LayerNorm weight gradients: per-block partial sums now, one batched
+    // fixed-order reduction of all 2L+1 LayerNorms after the layer loop
+    LnRedBatch ln_red;
+    ln_red.count = 0;
     {
         KScope k(h, K_LAYERNORM_BWD, ln_bytes(false));
-        layernorm_bwd<T>(R(0), nullptr, G[P_LNFW], G[P_LNFB], dC, res3 + (L - 1) * nC, P[P_LNFW],
-                         (float*)h->a[A_LNF_MEAN], (float*)h->a[A_LNF_RSTD], BT, C, lnp, st);
+        layernorm_bwd_rows<T>(R(0), nullptr, dC, res3 + (L - 1) * nC, P[P_LNFW],
+                              (float*)h->a[A_LNF_MEAN], (float*)h->a[A_LNF_RSTD], BT, C, lnp,
+                              ln_red.count, st);
+        ln_red.t[ln_red.count++] = {G[P_LNFW], G[P_LNFB]};
     }
     for (int l = L - 1; l >= 0; l--) {
         const T* res = l == 0 ? encoded : res3 + (l - 1) * nC;
@@ -436,9 +442,10 @@ void backward_impl(gpt2* h) {
         dw_tasks.push_back({d4C, ln2 + l * nC, G[P_FCW] + w4, G[P_FCB] + l * 4 * C, 4 * C, C});
         {
             KScope k(h, K_LAYERNORM_BWD, ln_bytes(true));
-            layernorm_bwd<T>(g1, g2, G[P_LN2W] + l * C, G[P_LN2B] + l * C, dC, res2 + l * nC,
-                             P[P_LN2W] + l * C, ln2m + (int64_t)l * BT, ln2r + (int64_t)l * BT,
-                             BT, C, lnp, st);
+            layernorm_bwd_rows<T>(g1, g2, dC, res2 + l * nC, P[P_LN2W] + l * C,
+                                  ln2m + (int64_t)l * BT, ln2r + (int64_t)l * BT, BT, C, lnp,
+                                  ln_red.count, st);
+            ln_red.t[ln_red.count++] = {G[P_LN2W] + l * C, G[P_LN2B] + l * C};
         }
         // attention
         const int64_t w1 = (int64_t)l * C * C, w3 = (int64_t)l * 3 * C * C;
@@ -459,12 +466,16 @@ void backward_impl(gpt2* h) {
         dw_tasks.push_back({d3C, ln1 + l * nC, G[P_QKVW] + w3, G[P_QKVB] + l * 3 * C, 3 * C, C});
         {
             KScope k(h, K_LAYERNORM_BWD, ln_bytes(true));
-            layernorm_bwd<T>(g0, g1, G[P_LN1W] + l * C, G[P_LN1B] + l * C, dC, res,
-                             P[P_LN1W] + l * C, ln1m + (int64_t)l * BT, ln1r + (int64_t)l * BT,
-                             BT, C, lnp, st);
+            layernorm_bwd_rows<T>(g0, g1, dC, res, P[P_LN1W] + l * C, ln1m + (int64_t)l * BT,
+                                  ln1r + (int64_t)l * BT, BT, C, lnp, ln_red.count, st);
+            ln_red.t[ln_red.count++] = {G[P_LN1W] + l * C, G[P_LN1B] + l * C};
         }
         dw_flops += mm_flops(C, 4 * C, BT) + mm_flops(4 * C, C, BT) + mm_flops(C, C, BT) +
                     mm_flops(3 * C, C, BT);
+    }
+    {
+        KScope k(h, K_LAYERNORM_BWD, (double)ln_red.count * layernorm_bwd_partials((int)C, 1) * 4);
+        layernorm_bwd_reduce(ln_red, BT, C, lnp, ln_red.count, st);
     }
     {
         KScope k(h, K_MATMUL_BWD_DW, dw_flops);

@@ -24,14 +24,29 @@ void encoder_bwd(float* dwte, float* dwpe, const T* dout, const int32_t* tok, in
 template <typename T>
 void layernorm_fwd(T* out, float* mean, float* rstd, const T* inp, const T* w, const T* b,
                    int N, int C, hipStream_t st);
-// dinp = dx (+ dadd[...] when dadd != nullptr; dadd may alias dinp); dw, db
-// are written (fp32). partials: fp32 workspace of layernorm_bwd_partials(C)
-// floats.
+// Backward in two parts. layernorm_bwd_rows: dinp = dx (+ dadd[...] when
+// dadd != nullptr; dadd may alias dinp), and the per-block partial sums of
+// dw, db into LayerNorm slot `slot` of the workspace. layernorm_bwd_reduce:
+// the dw, db of slots 0 .. b.count-1 (task i writes slot i's sums), summed
+// in a fixed order, all in two launches. partials: fp32 workspace of
+// layernorm_bwd_partials(C, count) floats; every slot of one reduce has the
+// same N.
+#define LN_RED_MAX 128
+struct LnRedTask {
+    float* dw;
+    float* db;
+};
+struct LnRedBatch {
+    int count;
+    LnRedTask t[LN_RED_MAX];
+};
 template <typename T>
-void layernorm_bwd(T* dinp, const T* dadd, float* dw, float* db, const T* dout, const T* inp,
-                   const T* w, const float* mean, const float* rstd, int N, int C,
-                   float* partials, hipStream_t st);
-int64_t layernorm_bwd_partials(int C);
+void layernorm_bwd_rows(T* dinp, const T* dadd, const T* dout, const T* inp, const T* w,
+                        const float* mean, const float* rstd, int N, int C, float* partials,
+                        int slot, hipStream_t st);
+void layernorm_bwd_reduce(const LnRedBatch& b, int N, int C, float* partials, int count,
+                          hipStream_t st);
+int64_t layernorm_bwd_partials(int C, int count);
 
 // ---- matmul -----------------------------------------------------------------
 // out[M,N] = inp[M,K] . w[N,K]^T (+ bias[N]) (+ residual[M,N])

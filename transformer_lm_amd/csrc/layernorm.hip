@@ -166,9 +166,14 @@ __global__ __launch_bounds__(256) void layernorm_bwd_kernel(
 // Stage 2 sums the LN_RED_GROUPS stage-1 rows of each column in order.
 #define LN_RED_GROUPS 16
 
+// Any number of LayerNorms at once (blockIdx.z selects one): each has its
+// partial rows at partials + z * LN_BWD_BLOCKS * 2C and its stage-1 rows at
+// stage + z * LN_RED_GROUPS * 2C.
 __global__ __launch_bounds__(256) void layernorm_bwd_reduce1_kernel(
     float* __restrict__ stage, const float* __restrict__ partials, int nblocks, int C) {
     __shared__ float red[4][64];
+    partials += (int64_t)blockIdx.z * LN_BWD_BLOCKS * 2 * C;
+    stage += (int64_t)blockIdx.z * LN_RED_GROUPS * 2 * C;
     const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
     const int j = blockIdx.x * 64 + tx;
     const int per = (nblocks + LN_RED_GROUPS - 1) / LN_RED_GROUPS;
@@ -182,10 +187,14 @@ __global__ __launch_bounds__(256) void layernorm_bwd_reduce1_kernel(
         stage[(int64_t)blockIdx.y * 2 * C + j] = ((red[0][tx] + red[1][tx]) + red[2][tx]) + red[3][tx];
 }
 
-__global__ __launch_bounds__(256) void layernorm_bwd_reduce2_kernel(
-    float* __restrict__ dw, float* __restrict__ db, const float* __restrict__ stage, int C) {
+__global__ __launch_bounds__(256) void layernorm_bwd_reduce2_kernel(const LnRedBatch b,
+                                                                   const float* __restrict__ stage,
+                                                                   int C) {
     const int j = blockIdx.x * blockDim.x + threadIdx.x;
     if (j >= 2 * C) return;
+    float* dw = b.t[blockIdx.y].dw;
+    float* db = b.t[blockIdx.y].db;
+    stage += (int64_t)blockIdx.y * LN_RED_GROUPS * 2 * C;
     float t = 0.f;
 #pragma unroll
     for (int r = 0; r < LN_RED_GROUPS; r++) t += stage[(int64_t)r * 2 * C + j];
@@ -195,34 +204,43 @@ __global__ __launch_bounds__(256) void layernorm_bwd_reduce2_kernel(
         db[j - C] = t;
 }
 
-// partial rows of the blocks, then the stage-1 rows
-int64_t layernorm_bwd_partials(int C) { return (int64_t)(LN_BWD_BLOCKS + LN_RED_GROUPS) * 2 * C; }
+// workspace of `count` LayerNorms: their partial rows, then their stage-1 rows
+int64_t layernorm_bwd_partials(int C, int count) {
+    return (int64_t)count * (LN_BWD_BLOCKS + LN_RED_GROUPS) * 2 * C;
+}
 
 template <typename T>
-void layernorm_bwd(T* dinp, const T* dadd, float* dw, float* db, const T* dout, const T* inp,
-                   const T* w, const float* mean, const float* rstd, int N, int C,
-                   float* partials, hipStream_t st) {
+void layernorm_bwd_rows(T* dinp, const T* dadd, const T* dout, const T* inp, const T* w,
+                        const float* mean, const float* rstd, int N, int C, float* partials,
+                        int slot, hipStream_t st) {
     int nb = ceil_div(N, LN_ROWS_PER_BLOCK);
     if (nb > LN_BWD_BLOCKS) nb = LN_BWD_BLOCKS;
+    partials += (int64_t)slot * LN_BWD_BLOCKS * 2 * C;
     if (C <= 1024)
         layernorm_bwd_kernel<T, 2><<<nb, 256, 0, st>>>(dinp, dadd, dout, inp, w, mean, rstd,
                                                        N, C, partials);
     else
         layernorm_bwd_kernel<T, 4><<<nb, 256, 0, st>>>(dinp, dadd, dout, inp, w, mean, rstd,
                                                        N, C, partials);
-    float* stage = partials + (int64_t)LN_BWD_BLOCKS * 2 * C;
-    layernorm_bwd_reduce1_kernel<<<dim3(ceil_div(2 * C, 64), LN_RED_GROUPS), 256, 0, st>>>(
-        stage, partials, nb, C);
-    layernorm_bwd_reduce2_kernel<<<ceil_div(2 * C, 256), 256, 0, st>>>(dw, db, stage, C);
+}
+
+void layernorm_bwd_reduce(const LnRedBatch& b, int N, int C, float* partials, int count,
+                          hipStream_t st) {
+    int nb = ceil_div(N, LN_ROWS_PER_BLOCK);
+    if (nb > LN_BWD_BLOCKS) nb = LN_BWD_BLOCKS;
+    float* stage = partials + (int64_t)count * LN_BWD_BLOCKS * 2 * C;
+    layernorm_bwd_reduce1_kernel<<<dim3(ceil_div(2 * C, 64), LN_RED_GROUPS, b.count), 256, 0,
+                                   st>>>(stage, partials, nb, C);
+    layernorm_bwd_reduce2_kernel<<<dim3(ceil_div(2 * C, 256), b.count), 256, 0, st>>>(b, stage, C);
 }
 
 template void layernorm_fwd<float>(float*, float*, float*, const float*, const float*,
                                    const float*, int, int, hipStream_t);
 template void layernorm_fwd<bf16>(bf16*, float*, float*, const bf16*, const bf16*, const bf16*,
                                   int, int, hipStream_t);
-template void layernorm_bwd<float>(float*, const float*, float*, float*, const float*, const float*,
-                                   const float*, const float*, const float*, int, int, float*,
-                                   hipStream_t);
-template void layernorm_bwd<bf16>(bf16*, const bf16*, float*, float*, const bf16*, const bf16*,
-                                  const bf16*, const float*, const float*, int, int, float*,
-                                  hipStream_t);
+template void layernorm_bwd_rows<float>(float*, const float*, const float*, const float*,
+                                        const float*, const float*, const float*, int, int, float*,
+                                        int, hipStream_t);
+template void layernorm_bwd_rows<bf16>(bf16*, const bf16*, const bf16*, const bf16*, const bf16*,
+                                       const float*, const float*, int, int, float*, int,
+                                       hipStream_t);

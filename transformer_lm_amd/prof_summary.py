@@ -122,7 +122,7 @@ def source_sha():
 def launches_per_step(L):
     return {"matmul_fwd": 4 * L + 1, "matmul_bwd_dx": 4 * L + 1, "matmul_bwd_dw": 2,
             "attention_fwd": L, "attention_bwd": L, "layernorm_fwd": 2 * L + 1,
-            "layernorm_bwd": 2 * L + 1, "gelu_fwd": L, "gelu_bwd": L, "classifier": 1,
+            "layernorm_bwd": 2 * L + 2, "gelu_fwd": L, "gelu_bwd": L, "classifier": 1,
             "encoder_fwd": 1, "encoder_bwd": 1, "adamw": 1}
 
 
