@@ -234,44 +234,16 @@ __global__ __launch_bounds__(256, 4) void flash_fwd_kernel(bf16* __restrict__ ou
     }
 }
 
-// ---------------------------------------------------- backward preparation --
-// Per (b, t, h): D = sum_d dO[d] O[d] (the softmax-backward correction of the
-// row) and the log-sum-exp in base 2. Eight lanes per row, 16 bytes each.
-__global__ __launch_bounds__(256) void flash_bwd_prep_kernel(float* __restrict__ Dbuf,
-                                                             float* __restrict__ lse2,
-                                                             const float* __restrict__ lse,
-                                                             const bf16* __restrict__ dout,
-                                                             const bf16* __restrict__ out,
-                                                             int Tn, int NH, int64_t rows) {
-    const int64_t row = (blockIdx.x * (int64_t)blockDim.x + threadIdx.x) >> 3;  // (b*Tn + t)*NH + h
-    const int j = threadIdx.x & 7;
-    float s = 0.f;
-    if (row < rows) {
-        const bf16x8 a = ld16(dout + row * HS + 8 * j);
-        const bf16x8 c = ld16(out + row * HS + 8 * j);
-#pragma unroll
-        for (int i = 0; i < 8; i++) s += (float)a[i] * (float)c[i];
-    }
-    s += __shfl_xor(s, 1, 64);
-    s += __shfl_xor(s, 2, 64);
-    s += __shfl_xor(s, 4, 64);
-    if (row < rows && j == 0) {
-        const int h = (int)(row % NH);
-        const int64_t bt = row / NH, b = bt / Tn, t = bt % Tn;
-        const int64_t i = (b * NH + h) * Tn + t;
-        Dbuf[i] = s;
-        lse2[i] = lse[i] * LOG2E;
-    }
-}
-
 // ------------------------------------------------------------ backward dK dV --
 // Block: 128 keys of one (b, h); wave w owns keys kw .. kw+31, lane l the key
 // kw + l%32. Per 64-query tile (queries >= the block's first key), in two
 // 32-query halves: S = Q K^T and dP = dO V^T (queries x keys),
-// P = exp2(S*c - lse2), dS = P (dP - D); dV^T += dO^T P; dK^T += Q^T dS.
+// P = exp2(S*c - lse*log2(e)), dS = P (dP - D); dV^T += dO^T P; dK^T += Q^T dS.
+// D = sum_d dO[d] O[d] per query (the softmax-backward correction of the
+// row) comes from the dQ kernel, which runs first.
 __global__ __launch_bounds__(256, 2) void flash_bwd_dkv_kernel(
     bf16* __restrict__ dqkv, const bf16* __restrict__ dout, const bf16* __restrict__ qkv,
-    const float* __restrict__ lse2, const float* __restrict__ Dbuf, int Tn, int C, int NH) {
+    const float* __restrict__ lse, const float* __restrict__ Dbuf, int Tn, int C, int NH) {
     extern __shared__ __attribute__((aligned(16))) bf16 ring[];
     auto Qs = [&](int i) { return ring + i * TILE_ELEMS; };
     auto Os = [&](int i) { return ring + (2 + i) * TILE_ELEMS; };
@@ -287,7 +259,7 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkv_kernel(
     const bf16* dbase = dout + (int64_t)b * Tn * C + h * HS;
     const auto rq = slice_rsrc(base);
     const auto ro = slice_rsrc(dbase);
-    const auto rl = slice_rsrc(wid == 2 ? lse2 + (int64_t)bh * Tn : Dbuf + (int64_t)bh * Tn);
+    const auto rl = slice_rsrc(wid == 2 ? lse + (int64_t)bh * Tn : Dbuf + (int64_t)bh * Tn);
     const int kb0 = kq * Q_PER_BLOCK;
     const int kw = kb0 + wid * 32;
     const int kl = kw + (lane & 31);
@@ -302,7 +274,7 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkv_kernel(
     floatx16 dk[2] = {floatx16{}, floatx16{}}, dv[2] = {floatx16{}, floatx16{}};
 
     // tile t covers queries kb0 + 64 t ..; the per-query statistics come along
-    // by direct loads (wave 2: base-2 log-sum-exp, wave 3: D), one float a lane
+    // by direct loads (wave 2: log-sum-exp, wave 3: D), one float a lane
     auto issue = [&](int t, int buf) {
         const int q0 = kb0 + t * TILE;
         dma_tile(Qs(buf), rq, 0, C3, q0, Tn, wid, lane);
@@ -339,7 +311,7 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkv_kernel(
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
                     const int v = 4 * r + e;
-                    float p = exp2_fast(fmaf(s[v], sc, -l4[e]));
+                    float p = exp2_fast(fmaf(s[v], sc, -(l4[e] * LOG2E)));
                     if (edge) {
                         const int q = q0 + qo + e;
                         p = (kl <= q && q < Tn) ? p : 0.f;
@@ -385,7 +357,8 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkv_kernel(
 // dS^T = P^T (dP^T - D); dQ^T += K^T dS^T.
 __global__ __launch_bounds__(256, 3) void flash_bwd_dq_kernel(
     bf16* __restrict__ dqkv, const bf16* __restrict__ dout, const bf16* __restrict__ qkv,
-    const float* __restrict__ lse2, const float* __restrict__ Dbuf, int Tn, int C, int NH) {
+    const bf16* __restrict__ out, const float* __restrict__ lse, float* __restrict__ Dbuf, int Tn,
+    int C, int NH) {
     extern __shared__ __attribute__((aligned(16))) bf16 ring[];
     auto Ks = [&](int i) { return ring + i * TILE_ELEMS; };
     auto Vs = [&](int i) { return ring + (2 + i) * TILE_ELEMS; };
@@ -407,8 +380,25 @@ __global__ __launch_bounds__(256, 3) void flash_bwd_dq_kernel(
         df[kb] = ql < Tn ? ld16(dout + ((int64_t)b * Tn + ql) * C + h * HS + kb * 16 + 8 * g)
                          : bf16x8{};
     }
-    const float l2 = ql < Tn ? lse2[(int64_t)bh * Tn + ql] : 0.f;
-    const float Dq = ql < Tn ? Dbuf[(int64_t)bh * Tn + ql] : 0.f;
+    const float l2 = ql < Tn ? lse[(int64_t)bh * Tn + ql] * LOG2E : 0.f;
+    // D = rowsum(dO o O) of this lane's query: 8-dim chunk sums (chunk 2 kb + g
+    // is here), then pairs of chunks, in a fixed tree; the dK/dV kernel,
+    // launched after this one, reads it from Dbuf
+    float Dq = 0.f;
+    {
+        float cs[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; kb++) {
+            const bf16x8 o = ql < Tn ? ld16(out + ((int64_t)b * Tn + ql) * C + h * HS + kb * 16 + 8 * g)
+                                     : bf16x8{};
+            float t = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; i++) t += (float)df[kb][i] * (float)o[i];
+            cs[kb] = t + __shfl_xor(t, 32, 64);
+        }
+        Dq = (cs[0] + cs[1]) + (cs[2] + cs[3]);
+        if (ql < Tn && g == 0) Dbuf[(int64_t)bh * Tn + ql] = Dq;
+    }
     floatx16 dq[2] = {floatx16{}, floatx16{}};
 
     const int ntiles = (min(Tn, (qt + 1) * Q_PER_BLOCK) + TILE - 1) / TILE;
@@ -475,18 +465,13 @@ void flash_attention_fwd(bf16* out, float* lse, const bf16* qkv, int B, int Tn, 
     flash_fwd_kernel<<<grid, 256, 4 * TILE_ELEMS * sizeof(bf16), st>>>(out, lse, qkv, Tn, C, NH);
 }
 
-// work: 2 * B*NH*Tn floats (D, then the base-2 log-sum-exp).
+// work: B*NH*Tn floats (D, written by the dQ kernel for the dK/dV kernel).
 void flash_attention_bwd(bf16* dqkv, const bf16* dout, const bf16* qkv, const bf16* out,
                          const float* lse, float* work, int B, int Tn, int C, int NH,
                          hipStream_t st) {
-    const int64_t rows = (int64_t)B * Tn * NH;
-    float* Dbuf = work;
-    float* lse2 = work + rows;
-    flash_bwd_prep_kernel<<<(unsigned)ceil_div(rows * 8, 256), 256, 0, st>>>(Dbuf, lse2, lse, dout,
-                                                                           out, Tn, NH, rows);
     const dim3 grid(ceil_div(Tn, Q_PER_BLOCK) * B * NH);
+    flash_bwd_dq_kernel<<<grid, 256, 4 * TILE_ELEMS * sizeof(bf16), st>>>(dqkv, dout, qkv, out, lse,
+                                                                         work, Tn, C, NH);
     flash_bwd_dkv_kernel<<<grid, 256, 4 * TILE_ELEMS * sizeof(bf16) + 4 * TILE * sizeof(float),
-                           st>>>(dqkv, dout, qkv, lse2, Dbuf, Tn, C, NH);
-    flash_bwd_dq_kernel<<<grid, 256, 4 * TILE_ELEMS * sizeof(bf16), st>>>(dqkv, dout, qkv, lse2,
-                                                                         Dbuf, Tn, C, NH);
+                           st>>>(dqkv, dout, qkv, lse, work, Tn, C, NH);
 }

@@ -141,7 +141,7 @@ void plan(const gpt2_config* c, Layout* lay) {
     a[W_DC] = BT * C * es;
     a[W_D3C] = L * BT * 3 * C * es;
     a[W_D4C] = L * BT * 4 * C * es;
-    a[W_ATT_D] = 2 * B * NH * T * 4;  // D, then the base-2 log-sum-exp
+    a[W_ATT_D] = B * NH * T * 4;  // attention backward's D rows
     a[W_LN_PART] = layernorm_bwd_partials((int)C, (int)(2 * L + 1)) * 4;
     a[W_BIAS_PART] = bias_bwd_partials((int)BT, (int)(4 * C)) * 4;
     a[W_ENC] = encoder_bwd_workspace_bytes((int)BT, (int)V, (int)C);

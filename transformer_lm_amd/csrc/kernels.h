@@ -110,8 +110,8 @@ bool gemm_bf16_bwd_dw_batch(const DwTask* tasks, int n, int M, hipStream_t st);
 template <typename T>
 void attention_fwd(T* out, float* lse, const T* qkv, int B, int Tn, int C, int NH,
                    hipStream_t st);
-// dqkv (B,T,3C) written; Dbuf: fp32 workspace (B,NH,T).
-// work: 2 * B * NH * Tn floats.
+// dqkv (B,T,3C) written; work: fp32 workspace of B * NH * Tn floats (the
+// rows' D = sum dO o O).
 template <typename T>
 void attention_bwd(T* dqkv, const T* dout, const T* qkv, const T* out, const float* lse,
                    float* work, int B, int Tn, int C, int NH, hipStream_t st);
