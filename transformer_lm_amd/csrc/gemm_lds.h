@@ -147,8 +147,8 @@ struct LdsOperand {
     }
 
     // Loads the tile at rows row0.., reduction k0.. into LDS at s, through
-    // inline asm (ASM) or the compiler builtin (see gemm_stream_kernel for
-    // which layout uses which).
+    // inline asm (ASM) or the compiler builtin (GemmLds says which launches
+    // use which).
     template <bool ASM>
     __device__ __forceinline__ void load(bf16* s, const bf16* __restrict__ g, int ld, int row0,
                                          int k0, int wid) const {
@@ -259,7 +259,7 @@ __device__ __forceinline__ void lds_barrier() {
 // epilogue's bias and residual loads) then count a subset of the operations in
 // flight and stay safe.
 template <int BM, int BN, int BK, int WM, int WN, int GM, int S, int OCC, bool XRC, bool YRC,
-          int EPI>
+          int EPI, bool ASM>
 __global__ __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_eu(OCC * WM * WN / 4)))
 void gemm_stream_kernel(const GemmGroup g) {
 #if __HIP_DEVICE_COMPILE__  // buffer builtins exist for the device pass only
@@ -285,11 +285,6 @@ void gemm_stream_kernel(const GemmGroup g) {
     static_assert(NW * 32 * SP * 4 <= SLOT * 2, "sub-tile staging fits one ring slot");
     constexpr int RSG = NT / (BM / 8);  // row sums: k groups of 16-byte column chunks
     static_assert(!XRC || (BK % RSG == 0 && RSG * BM * 4 <= SLOT * 2), "row-sum layout");
-    // The transpose reads of the dx and dW layouts need the inline-asm loads:
-    // builtin loads make the compiler wait for all of them before every such
-    // read (it cannot tell which LDS bytes a read touches). The forward layout
-    // reads with ds_read_b128, which the compiler keeps apart from the loads.
-    constexpr bool ASM = YRC;
     extern __shared__ __attribute__((aligned(16))) bf16 lds_ring[];
 
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -564,7 +559,12 @@ void gemm_stream_kernel(const GemmGroup g) {
 }
 
 // Launch helper for one tile shape: the grid is min(total tiles, OCC blocks
-// per CU on 256 CUs).
+// per CU on 256 CUs). ASM selects the LDS loads' form. With builtin loads the
+// compiler waits for all of them before every transpose read (it cannot tell
+// which LDS bytes a read touches), so the inline-asm form is the default for
+// layouts with transpose reads; measured, the grouped weight gradients still
+// run faster with the builtin form (that wait is cheap behind their bias
+// sums' LDS reads), the lm-head's single one with the asm form.
 template <int BM, int BN, int BK, int WM, int WN, int GM, int S, int OCC>
 struct GemmLds {
     static constexpr int bm = BM, bn = BN, bk = BK, slots = OCC * 256;
@@ -572,19 +572,19 @@ struct GemmLds {
 
     static int tiles(int M, int N) { return ceil_div(M, BM) * ceil_div(N, BN); }
 
-    template <bool XRC, bool YRC, int EPI>
+    template <bool XRC, bool YRC, int EPI, bool ASM = YRC>
     static void run(const GemmGroup& g, hipStream_t st) {
         const int total = g.first_tile[g.count];
         const int grid = total < slots ? total : slots;
-        gemm_stream_kernel<BM, BN, BK, WM, WN, GM, S, OCC, XRC, YRC, EPI>
+        gemm_stream_kernel<BM, BN, BK, WM, WN, GM, S, OCC, XRC, YRC, EPI, ASM>
             <<<grid, WM * WN * 64, lds_bytes, st>>>(g);
     }
 
     // Raises the kernel's dynamic-LDS limit (needed above 64 KB); call once.
-    template <bool XRC, bool YRC, int EPI>
+    template <bool XRC, bool YRC, int EPI, bool ASM = YRC>
     static hipError_t prepare() {
         return hipFuncSetAttribute(
-            (const void*)gemm_stream_kernel<BM, BN, BK, WM, WN, GM, S, OCC, XRC, YRC, EPI>,
+            (const void*)gemm_stream_kernel<BM, BN, BK, WM, WN, GM, S, OCC, XRC, YRC, EPI, ASM>,
             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
     }
 };
