@@ -17,9 +17,9 @@ from collections import defaultdict
 
 # kernel symbol (substring) -> library timing class
 CLASSES = [
-    (r"gemm_(lds|mfma|persistent)_kernel<[^>]*false, false", "matmul_fwd"),
-    (r"gemm_(lds|mfma|persistent)_kernel<[^>]*false, true", "matmul_bwd_dx"),
-    (r"gemm_(lds|mfma|persistent)_kernel<[^>]*true, true", "matmul_bwd_dw"),
+    (r"gemm_(lds|mfma|persistent|stream)_kernel<[^>]*false, false", "matmul_fwd"),
+    (r"gemm_(lds|mfma|persistent|stream)_kernel<[^>]*false, true", "matmul_bwd_dx"),
+    (r"gemm_(lds|mfma|persistent|stream)_kernel<[^>]*true, true", "matmul_bwd_dw"),
     (r"split_reduce_kernel", "matmul_bwd_dw"),
     (r"flash_fwd_kernel|attention_fwd_rows", "attention_fwd"),
     (r"flash_bwd|attention_bwd", "attention_bwd"),
@@ -31,7 +31,7 @@ CLASSES = [
     (r"encoder_fwd", "encoder_fwd"),
     (r"encoder_bwd|token_|enc_(rank|scan|fill|range|fix)", "encoder_bwd"),
     (r"fill_zero_kernel<int>", "encoder_bwd"),
-    (r"adamw", "adamw"),
+    (r"adamw|grad_norm", "adamw"),
 ]
 
 
