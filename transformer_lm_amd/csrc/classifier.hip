@@ -84,6 +84,24 @@ struct Chunk8 {
     }
 };
 
+// The row is read once and overwritten once: non-temporal accesses keep it
+// from displacing other data in the caches.
+template <typename T>
+__device__ __forceinline__ Chunk8<T> load_chunk_nt(const T* p) {
+    typedef unsigned int u32v __attribute__((ext_vector_type(sizeof(T) * 2)));
+    Chunk8<T> c;
+    *reinterpret_cast<u32v*>(c.x) = __builtin_nontemporal_load(reinterpret_cast<const u32v*>(p));
+    return c;
+}
+template <typename T>
+__device__ __forceinline__ void store8_nt(T* p, const float (&v)[8]) {
+    typedef unsigned int u32v __attribute__((ext_vector_type(sizeof(T) * 2)));
+    typename Vec8<T>::raw r;
+#pragma unroll
+    for (int i = 0; i < 8; i++) r[i] = from_f32<T>(v[i]);
+    __builtin_nontemporal_store(__builtin_bit_cast(u32v, r), reinterpret_cast<u32v*>(p));
+}
+
 template <typename T, int NCHK>
 __global__ __launch_bounds__(CL_THREADS) __attribute__((amdgpu_waves_per_eu(4))) void classifier_reg_kernel(
     T* logits, float* __restrict__ losses, const int32_t* __restrict__ targets, int V, int Vp,
@@ -97,7 +115,7 @@ __global__ __launch_bounds__(CL_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
 #pragma unroll
     for (int k = 0; k < NCHK; k++) {
         const int c = (threadIdx.x + k * CL_THREADS) * 8;
-        if (c < Vp) v[k] = *reinterpret_cast<const Chunk8<T>*>(z + c);
+        if (c < Vp) v[k] = load_chunk_nt(z + c);
     }
     float m = -INFINITY, s = 0.f;
 #pragma unroll
@@ -145,7 +163,7 @@ __global__ __launch_bounds__(CL_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
                                      dloss
                                : 0.f;
             }
-            store8(z + c, d);
+            store8_nt(z + c, d);
         }
     }
 }
