@@ -30,6 +30,8 @@
 // the register budgets that fit keep every kernel free of spills, and the
 // extra waves hide the matrix-core / exponential / LDS latencies of each
 // wave's serial tile loop.
+#include <type_traits>
+
 #include "gemm_lds.h"
 
 #define HS 64
@@ -292,46 +294,53 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkv_kernel(
         tile_barrier();
         if (t + 1 < ntiles) issue(t + 1, buf ^ 1);
         if (kw > q0 + TILE - 1 || kw >= Tn) continue;  // no query of the tile sees these keys
-        const bool edge = q0 < kw + 31 || q0 + TILE > Tn;  // wave-uniform
         const bf16* qs = Qs(buf);
         const bf16* os = Os(buf);
+        // the tile body, compiled once with the causal / end-of-sequence mask
+        // and once without it (tiles clear of the diagonal and the end)
+        auto tile = [&](auto masked) {
 #pragma unroll
-        for (int qt = 0; qt < 2; qt++) {
-            floatx16 s = floatx16{}, dp = floatx16{};
+            for (int qt = 0; qt < 2; qt++) {
+                floatx16 s = floatx16{}, dp = floatx16{};
 #pragma unroll
-            for (int kb = 0; kb < 4; kb++) {
-                s = mfma(frag_rows(qs, 32 * qt, kb, lane), kf[kb], s);
-                dp = mfma(frag_rows(os, 32 * qt, kb, lane), vf[kb], dp);
-            }
+                for (int kb = 0; kb < 4; kb++) {
+                    s = mfma(frag_rows(qs, 32 * qt, kb, lane), kf[kb], s);
+                    dp = mfma(frag_rows(os, 32 * qt, kb, lane), vf[kb], dp);
+                }
 #pragma unroll
-            for (int r = 0; r < 4; r++) {
-                const int qo = 32 * qt + 8 * r + 4 * g;  // 4 consecutive queries
-                const floatx4 l4 = *reinterpret_cast<const floatx4*>(&ls(buf)[qo]);
-                const floatx4 d4 = *reinterpret_cast<const floatx4*>(&Ds(buf)[qo]);
+                for (int r = 0; r < 4; r++) {
+                    const int qo = 32 * qt + 8 * r + 4 * g;  // 4 consecutive queries
+                    const floatx4 l4 = *reinterpret_cast<const floatx4*>(&ls(buf)[qo]);
+                    const floatx4 d4 = *reinterpret_cast<const floatx4*>(&Ds(buf)[qo]);
 #pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    const int v = 4 * r + e;
-                    float p = exp2_fast(fmaf(s[v], sc, -(l4[e] * LOG2E)));
-                    if (edge) {
-                        const int q = q0 + qo + e;
-                        p = (kl <= q && q < Tn) ? p : 0.f;
+                    for (int e = 0; e < 4; e++) {
+                        const int v = 4 * r + e;
+                        float p = exp2_fast(fmaf(s[v], sc, -(l4[e] * LOG2E)));
+                        if constexpr (decltype(masked)::value) {
+                            const int q = q0 + qo + e;
+                            p = (kl <= q && q < Tn) ? p : 0.f;
+                        }
+                        s[v] = p;
+                        dp[v] = p * (dp[v] - d4[e]);
                     }
-                    s[v] = p;
-                    dp[v] = p * (dp[v] - d4[e]);
+                }
+#pragma unroll
+                for (int hh = 0; hh < 2; hh++) {
+                    const bf16x8 pb = half_tile(s, hh);
+                    const bf16x8 db = half_tile(dp, hh);
+                    const int rb = 32 * qt + 16 * hh;
+#pragma unroll
+                    for (int dt = 0; dt < 2; dt++) {
+                        dv[dt] = mfma(frag_dims(os, 32 * dt, rb, lane), pb, dv[dt]);
+                        dk[dt] = mfma(frag_dims(qs, 32 * dt, rb, lane), db, dk[dt]);
+                    }
                 }
             }
-#pragma unroll
-            for (int hh = 0; hh < 2; hh++) {
-                const bf16x8 pb = half_tile(s, hh);
-                const bf16x8 db = half_tile(dp, hh);
-                const int rb = 32 * qt + 16 * hh;
-#pragma unroll
-                for (int dt = 0; dt < 2; dt++) {
-                    dv[dt] = mfma(frag_dims(os, 32 * dt, rb, lane), pb, dv[dt]);
-                    dk[dt] = mfma(frag_dims(qs, 32 * dt, rb, lane), db, dk[dt]);
-                }
-            }
-        }
+        };
+        if (q0 < kw + 31 || q0 + TILE > Tn)  // wave-uniform
+            tile(std::true_type{});
+        else
+            tile(std::false_type{});
     }
     if (kl < Tn) {
         bf16* krow = dqkv + ((int64_t)b * Tn + kl) * C3 + C + h * HS;
@@ -355,7 +364,7 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkv_kernel(
 // Block: 128 queries; wave w owns queries q0 .. q0+31, lane l the query
 // q0 + l%32. Per 64-key tile: S^T = K Q^T, dP^T = V dO^T (keys x queries),
 // dS^T = P^T (dP^T - D); dQ^T += K^T dS^T.
-__global__ __launch_bounds__(256, 3) void flash_bwd_dq_kernel(
+__global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(
     bf16* __restrict__ dqkv, const bf16* __restrict__ dout, const bf16* __restrict__ qkv,
     const bf16* __restrict__ out, const float* __restrict__ lse, float* __restrict__ Dbuf, int Tn,
     int C, int NH) {
@@ -412,34 +421,41 @@ __global__ __launch_bounds__(256, 3) void flash_bwd_dq_kernel(
             dma_tile(Vs(buf ^ 1), rs, 4 * C, C3, k0 + TILE, Tn, wid, lane);
         }
         if (k0 > q0 + 31 || q0 >= Tn) continue;
-        const bool edge = k0 + TILE - 1 > q0 || k0 + TILE > Tn;  // wave-uniform
         const bf16* ks = Ks(buf);
         const bf16* vs = Vs(buf);
+        // the tile body, compiled once with the causal / end-of-sequence mask
+        // and once without it (tiles clear of the diagonal and the end)
+        auto tile = [&](auto masked) {
 #pragma unroll
-        for (int kt = 0; kt < 2; kt++) {
-            floatx16 s = floatx16{}, dp = floatx16{};
+            for (int kt = 0; kt < 2; kt++) {
+                floatx16 s = floatx16{}, dp = floatx16{};
 #pragma unroll
-            for (int kb = 0; kb < 4; kb++) {
-                s = mfma(frag_rows(ks, 32 * kt, kb, lane), qf[kb], s);
-                dp = mfma(frag_rows(vs, 32 * kt, kb, lane), df[kb], dp);
-            }
-#pragma unroll
-            for (int v = 0; v < 16; v++) {
-                float p = exp2_fast(fmaf(s[v], sc, -l2));
-                if (edge) {
-                    const int key = k0 + 32 * kt + 8 * (v >> 2) + 4 * g + (v & 3);
-                    p = (key <= ql && key < Tn) ? p : 0.f;
+                for (int kb = 0; kb < 4; kb++) {
+                    s = mfma(frag_rows(ks, 32 * kt, kb, lane), qf[kb], s);
+                    dp = mfma(frag_rows(vs, 32 * kt, kb, lane), df[kb], dp);
                 }
-                dp[v] = p * (dp[v] - Dq);
-            }
 #pragma unroll
-            for (int hh = 0; hh < 2; hh++) {
-                const bf16x8 db = half_tile(dp, hh);
+                for (int v = 0; v < 16; v++) {
+                    float p = exp2_fast(fmaf(s[v], sc, -l2));
+                    if constexpr (decltype(masked)::value) {
+                        const int key = k0 + 32 * kt + 8 * (v >> 2) + 4 * g + (v & 3);
+                        p = (key <= ql && key < Tn) ? p : 0.f;
+                    }
+                    dp[v] = p * (dp[v] - Dq);
+                }
 #pragma unroll
-                for (int dt = 0; dt < 2; dt++)
-                    dq[dt] = mfma(frag_dims(ks, 32 * dt, 32 * kt + 16 * hh, lane), db, dq[dt]);
+                for (int hh = 0; hh < 2; hh++) {
+                    const bf16x8 db = half_tile(dp, hh);
+#pragma unroll
+                    for (int dt = 0; dt < 2; dt++)
+                        dq[dt] = mfma(frag_dims(ks, 32 * dt, 32 * kt + 16 * hh, lane), db, dq[dt]);
+                }
             }
-        }
+        };
+        if (k0 + TILE - 1 > q0 || k0 + TILE > Tn)  // wave-uniform
+            tile(std::true_type{});
+        else
+            tile(std::false_type{});
     }
     if (ql < Tn) {
         bf16* qrow = dqkv + ((int64_t)b * Tn + ql) * C3 + h * HS;
