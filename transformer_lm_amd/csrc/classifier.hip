@@ -102,6 +102,9 @@ __device__ __forceinline__ void store8_nt(T* p, const float (&v)[8]) {
     __builtin_nontemporal_store(__builtin_bit_cast(u32v, r), reinterpret_cast<u32v*>(p));
 }
 
+// Chunks wholly inside the V real columns (all but at most one per row) take
+// a path without per-column tests; the chunk holding the target also yields
+// the target's logit from registers, and its lane writes the row's loss.
 template <typename T, int NCHK>
 __global__ __launch_bounds__(CL_THREADS) __attribute__((amdgpu_waves_per_eu(4))) void classifier_reg_kernel(
     T* logits, float* __restrict__ losses, const int32_t* __restrict__ targets, int V, int Vp,
@@ -117,11 +120,21 @@ __global__ __launch_bounds__(CL_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
         const int c = (threadIdx.x + k * CL_THREADS) * 8;
         if (c < Vp) v[k] = load_chunk_nt(z + c);
     }
-    float m = -INFINITY, s = 0.f;
+    float m = -INFINITY, s = 0.f, zt = 0.f;
 #pragma unroll
     for (int k = 0; k < NCHK; k++) {
         const int c = (threadIdx.x + k * CL_THREADS) * 8;
-        if (c < V) {
+        if (c + 8 <= V) {
+            float cm = fmaxf(fmaxf(fmaxf(v[k][0], v[k][1]), fmaxf(v[k][2], v[k][3])),
+                             fmaxf(fmaxf(v[k][4], v[k][5]), fmaxf(v[k][6], v[k][7])));
+            cm = fmaxf(cm, m);
+            const float cl = cm * CL_LOG2E;
+            float cs = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; i++) cs += __builtin_amdgcn_exp2f(fmaf(v[k][i], CL_LOG2E, -cl));
+            s = s * __builtin_amdgcn_exp2f((m - cm) * CL_LOG2E) + cs;
+            m = cm;
+        } else if (c < V) {
             float cm = m;
 #pragma unroll
             for (int i = 0; i < 8; i++)
@@ -134,26 +147,36 @@ __global__ __launch_bounds__(CL_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
             s = s * __builtin_amdgcn_exp2f((m - cm) * CL_LOG2E) + cs;
             m = cm;
         }
+        if (tgt >= c && tgt < c + 8) {
+#pragma unroll
+            for (int i = 0; i < 8; i++)
+                if (tgt == c + i) zt = v[k][i];
+        }
     }
 #pragma unroll
     for (int k = 0; k < NCHK; k++) v[k].launder();
     const float M = block_max(m, red);
     const float S = block_sum(m == -INFINITY ? 0.f : s * __builtin_amdgcn_exp2f((m - M) * CL_LOG2E), red);
     const float lse = M + logf(S);
-    if (threadIdx.x == 0) {
-        if (ok) {
-            losses[row] = lse - to_f32(z[tgt]);
-        } else {
-            losses[row] = 0.f;
-            atomicOr(err, 1);
-        }
+    // the lane holding the target column writes the loss (ok: tgt < V <= Vp)
+    if (ok) {
+        const int own = (tgt >> 3) % CL_THREADS;
+        if ((int)threadIdx.x == own) losses[row] = lse - zt;
+    } else if (threadIdx.x == 0) {
+        losses[row] = 0.f;
+        atomicOr(err, 1);
     }
-    __syncthreads();  // the target logit is read before any thread overwrites it
     const float l2 = lse * CL_LOG2E;
 #pragma unroll
     for (int k = 0; k < NCHK; k++) {
         const int c = (threadIdx.x + k * CL_THREADS) * 8;
-        if (c < Vp) {
+        if (c + 8 <= V && !(tgt >= c && tgt < c + 8)) {
+            float d[8];
+#pragma unroll
+            for (int i = 0; i < 8; i++)
+                d[i] = __builtin_amdgcn_exp2f(fmaf(v[k][i], CL_LOG2E, -l2)) * dloss;
+            store8_nt(z + c, d);
+        } else if (c < Vp) {
             float d[8];
 #pragma unroll
             for (int i = 0; i < 8; i++) {
