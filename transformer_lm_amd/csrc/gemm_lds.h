@@ -214,7 +214,7 @@ struct LdsOperand {
 // cursor runs S-1 stages ahead of the products, across tile boundaries, so the
 // next tile's first stages load while the current tile finishes and while its
 // epilogue drains.
-#define GROUP_MAX 48
+#define GROUP_MAX 52  // the 4 weight gradients of 12 layers and the tied output head
 // Cache policy of the epilogue's buffer stores: non-temporal (nt), so the
 // written outputs do not displace the operand panels that the L2 serves to
 // the other tiles.
@@ -234,6 +234,7 @@ struct GemmGroup {
     int first_tile[GROUP_MAX + 1];  // prefix sums of the problems' tile counts
     GemmProblem p[GROUP_MAX];
 };
+static_assert(sizeof(GemmGroup) <= 4096, "a group travels as one kernel argument");
 
 #if __HIP_DEVICE_COMPILE__
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t store_rsrc(void* base, int64_t bytes) {

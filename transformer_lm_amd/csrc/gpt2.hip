@@ -388,18 +388,21 @@ void backward_impl(gpt2* h) {
     // alternately d/d(x1) and d/d(input) of blocks L-1, L-2, ..., 0
     auto R = [&](int k) { return dres + (int64_t)k * nC; };
     std::vector<DwTask> dw_tasks;
-    dw_tasks.reserve(4 * L);
+    dw_tasks.reserve(4 * L + 1);
     double dw_flops = 0.0;
 
-    // output head (tied to wte): dlnf = dz . wte; dwte = dz^T . lnf
+    // output head (tied to wte): dlnf = dz . wte now; dwte = dz^T . lnf joins
+    // the layers' weight gradients in the grouped launch after the layer loop
+    // (the logits buffer holds dz until then; the encoder's token gradient is
+    // added to dwte after it). Every weight-gradient tile there reduces over
+    // the same B*T rows, so one launch fills the GPU's rounds of resident
+    // tiles better than two.
     {
         KScope k(h, K_MATMUL_BWD_DX, mm_flops(BT, C, Vp));
         matmul_bwd_dx<T>(dC, dlogits, P[P_WTE], BT, Vp, C, st);
     }
-    {
-        KScope k(h, K_MATMUL_BWD_DW, mm_flops(Vp, C, BT));
-        matmul_bwd_dw<T>(G[P_WTE], nullptr, dlogits, lnf, BT, Vp, C, dws, bp, st);
-    }
+    dw_tasks.push_back({dlogits, lnf, G[P_WTE], nullptr, Vp, C});
+    dw_flops += mm_flops(Vp, C, BT);
     // LayerNorm weight gradients: per-block partial sums now, one batched
     // fixed-order reduction of all 2L+1 LayerNorms after the layer loop
     LnRedBatch ln_red;

@@ -118,9 +118,9 @@ def source_sha():
 
 
 # timed launches of each class in one training step (L layers); the weight
-# gradients are two: the lm-head's, then those of all layers as one group
+# gradients of all layers and the output head run as one timed group
 def launches_per_step(L):
-    return {"matmul_fwd": 4 * L + 1, "matmul_bwd_dx": 4 * L + 1, "matmul_bwd_dw": 2,
+    return {"matmul_fwd": 4 * L + 1, "matmul_bwd_dx": 4 * L + 1, "matmul_bwd_dw": 1,
             "attention_fwd": L, "attention_bwd": L, "layernorm_fwd": 2 * L + 1,
             "layernorm_bwd": 2 * L + 2, "gelu_fwd": L, "gelu_bwd": L, "classifier": 1,
             "encoder_fwd": 1, "encoder_bwd": 1, "adamw": 1}
