@@ -413,6 +413,88 @@ double oracle_lr_schedule(double lr_max, double lr_min, int warmup, int total, i
 }
 
 /* ------------------------------------------------------------------------ */
+/* FP8 matrix products.                                                     */
+/* ------------------------------------------------------------------------ */
+/* The talk "llm.c's Origin and the Future of LLM Compilers", chapter
+ * "Project Roadmap, Community Forks, and LLaMA Architecture Support", names
+ * FP8 support as a direction and fixes nothing more. Plain readings, which the
+ * GPU path follows:
+ *   - format: the OCP 8-bit E4M3 format: sign, 4 exponent bits with bias 7,
+ *     3 mantissa bits; exponent field 0 holds the subnormals m/8 * 2^-6;
+ *     no infinities; codes 0x7f and 0xff are NaN; largest finite 448;
+ *   - conversion of a float: round to nearest, ties to the even code, not
+ *     saturating: magnitudes above 464 (the midpoint between 448 and the
+ *     unrepresentable 480) give NaN;
+ *   - per-tensor scaling: s = 448 / amax(|x|) computed in fp32 (s = 1 for an
+ *     all-zero tensor), q = E4M3(x * s) with the product rounded to fp32
+ *     first -- the precision the codes are decided in;
+ *   - product: out[i][j] = (sum_k dec(qx[i][k]) dec(qw[j][k])) / (sx sw)
+ *     + bias[j], the sum taken exactly (every product of two E4M3 values is a
+ *     multiple of 2^-18 below 2^17, so a double sum of up to 2^18 of them is
+ *     exact). */
+
+/* Value of an E4M3 code. */
+double oracle_e4m3_decode(int code) {
+    const int sgn = code & 0x80, e = (code >> 3) & 15, m = code & 7;
+    if (e == 15 && m == 7) return NAN;
+    const double mag = e == 0 ? ldexp((double)m / 8.0, -6) : ldexp(1.0 + m / 8.0, e - 7);
+    return sgn ? -mag : mag;
+}
+
+/* Code of the E4M3 value nearest to y (ties to the even code), by comparison
+ * with every finite non-negative code. */
+int oracle_e4m3_encode(float y) {
+    if (isnan(y)) return 0x7f;
+    const int sgn = signbit(y) ? 0x80 : 0;
+    const double a = fabs((double)y);
+    if (a > 464.0) return sgn | 0x7f;
+    int best = 0;
+    double bd = a;  /* distance to code 0 */
+    for (int c = 1; c <= 0x7e; c++) {
+        const double d = fabs(a - oracle_e4m3_decode(c));
+        if (d < bd || (d == bd && (c & 1) == 0 && (best & 1) == 1)) {
+            bd = d;
+            best = c;
+        }
+    }
+    return sgn | best;
+}
+
+/* Per-tensor scale of a tensor with largest magnitude amax. */
+float oracle_fp8_scale(float amax) { return amax > 0.0f ? 448.0f / amax : 1.0f; }
+
+/* Largest |x_i| over n floats. */
+float oracle_fp8_amax(const float* x, int64_t n) {
+    float m = 0.0f;
+    for (int64_t i = 0; i < n; i++) m = fabsf(x[i]) > m ? fabsf(x[i]) : m;
+    return m;
+}
+
+/* q_i = E4M3(x_i * s), the product rounded to fp32. */
+void oracle_fp8_quantize(unsigned char* q, const float* x, int64_t n, float s) {
+    for (int64_t i = 0; i < n; i++) {
+        volatile float p = x[i] * s;  /* one fp32 rounding, no contraction */
+        q[i] = (unsigned char)oracle_e4m3_encode(p);
+    }
+}
+
+/* out[M][N] = (qx[M][K] . qw[N][K]^T) / (sx sw) + bias[N] (bias may be NULL). */
+void oracle_fp8_matmul(double* out, const unsigned char* qx, const unsigned char* qw,
+                       const double* bias, int M, int N, int K, float sx, float sw) {
+    double dec[256];
+    for (int c = 0; c < 256; c++) dec[c] = oracle_e4m3_decode(c);
+    const double inv = 1.0 / ((double)sx * (double)sw);
+#pragma omp parallel for
+    for (int i = 0; i < M; i++)
+        for (int j = 0; j < N; j++) {
+            double acc = 0.0;
+            for (int k = 0; k < K; k++)
+                acc += dec[qx[(int64_t)i * K + k]] * dec[qw[(int64_t)j * K + k]];
+            out[(int64_t)i * N + j] = acc * inv + (bias ? bias[j] : 0.0);
+        }
+}
+
+/* ------------------------------------------------------------------------ */
 /* The model.                                                               */
 /* ------------------------------------------------------------------------ */
 

@@ -88,6 +88,14 @@ def load(precision="f64"):
         "oracle_adamw_scaled": (None, [R, R, R, R, ct.c_int64, real, real, real, real, real,
                                        ct.c_int, real]),
         "oracle_grad_norm": (real, [R, ct.c_int64]),
+        "oracle_e4m3_decode": (ct.c_double, [ct.c_int]),
+        "oracle_e4m3_encode": (ct.c_int, [ct.c_float]),
+        "oracle_fp8_scale": (ct.c_float, [ct.c_float]),
+        "oracle_fp8_amax": (ct.c_float, [ct.POINTER(ct.c_float), ct.c_int64]),
+        "oracle_fp8_quantize": (None, [ct.POINTER(ct.c_ubyte), ct.POINTER(ct.c_float),
+                                       ct.c_int64, ct.c_float]),
+        "oracle_fp8_matmul": (None, [D, ct.POINTER(ct.c_ubyte), ct.POINTER(ct.c_ubyte), D,
+                                     ct.c_int, ct.c_int, ct.c_int, ct.c_float, ct.c_float]),
         "oracle_lr_schedule": (ct.c_double, [ct.c_double, ct.c_double, ct.c_int, ct.c_int,
                                              ct.c_int]),
         "oracle_update_scheduled": (ct.c_double, [P, ct.c_double, ct.c_double, ct.c_int,
@@ -219,4 +227,55 @@ def fd_grads(w, params, inputs, targets, h=1e-5, start=0, count=None, precision=
                              ptr(targets, ct.c_int), h, start, count, ptr(out, ct.c_double))
     if rc:
         raise ValueError("token id outside [0, V)")
+    return out
+
+
+# ---- FP8 (E4M3) products: the oracle's functions over numpy arrays ----------
+
+def e4m3_decode(codes):
+    """Values (float64) of E4M3 codes (any integer array)."""
+    lib = load()
+    return np.array([lib.oracle_e4m3_decode(int(c)) for c in np.ravel(codes)]).reshape(
+        np.shape(codes))
+
+
+def e4m3_encode(x):
+    """E4M3 codes (uint8) of float32 values, one at a time."""
+    lib = load()
+    x = np.asarray(x, np.float32)
+    return np.array([lib.oracle_e4m3_encode(float(v)) for v in np.ravel(x)],
+                    np.uint8).reshape(x.shape)
+
+
+def fp8_amax(x):
+    lib = load()
+    x = np.ascontiguousarray(x, np.float32).ravel()
+    return lib.oracle_fp8_amax(ptr(x, ct.c_float), x.size)
+
+
+def fp8_scale(amax):
+    return load().oracle_fp8_scale(float(amax))
+
+
+def fp8_quantize(x, s):
+    """E4M3(x * s) codes, the product rounded to fp32."""
+    lib = load()
+    x = np.ascontiguousarray(x, np.float32)
+    q = np.empty(x.shape, np.uint8)
+    lib.oracle_fp8_quantize(ptr(q, ct.c_ubyte), ptr(x, ct.c_float), x.size, float(s))
+    return q
+
+
+def fp8_matmul(qx, qw, sx, sw, bias=None):
+    """(dec(qx) . dec(qw)^T) / (sx sw) + bias, float64 [M, N]."""
+    lib = load()
+    qx = np.ascontiguousarray(qx, np.uint8)
+    qw = np.ascontiguousarray(qw, np.uint8)
+    M, K = qx.shape
+    N = qw.shape[0]
+    assert qw.shape[1] == K
+    out = np.empty((M, N), np.float64)
+    b = None if bias is None else np.ascontiguousarray(bias, np.float64)
+    lib.oracle_fp8_matmul(ptr(out, ct.c_double), ptr(qx, ct.c_ubyte), ptr(qw, ct.c_ubyte),
+                          ptr(b, ct.c_double), M, N, K, float(sx), float(sw))
     return out

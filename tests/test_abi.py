@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(g):
     names = declared_functions()
-    assert len(names) == 21
+    assert len(names) == 25
     lib = ct.CDLL(g.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -97,3 +97,24 @@ def test_null_handle_calls_fail_cleanly(g):
     assert g._lib.gpt2_checkpoint_save(None, 1, None, 0) == g.GPT2_EINVAL
     assert g._lib.gpt2_checkpoint_load(None, None, 0, None) == g.GPT2_EINVAL
     g._lib.gpt2_free(None)
+
+
+def test_fp8_entry_points_validate_before_launching(g):
+    lib = g._lib
+    a = 1 << 20                                      # 16-byte aligned, never dereferenced
+    assert g.fp8_scale_workspace_bytes() >= 4
+    assert lib.gpt2_fp8_scale(None, a, a, 10, None) == g.GPT2_EINVAL
+    assert lib.gpt2_fp8_scale(a, a, a, -1, None) == g.GPT2_EINVAL
+    assert lib.gpt2_fp8_scale(a, a, a + 2, 10, None) == g.GPT2_EINVAL      # x misaligned
+    assert lib.gpt2_fp8_quantize(None, a, a, 10, None) == g.GPT2_EINVAL
+    assert lib.gpt2_fp8_quantize(a + 8, a, a, 10, None) == g.GPT2_EINVAL  # q misaligned
+    assert lib.gpt2_fp8_quantize(a, a, a, 0, None) == g.GPT2_OK           # empty: no launch
+    mm = lib.gpt2_fp8_matmul
+    assert mm(None, a, a, a, None, 8, 8, 128, None) == g.GPT2_EINVAL
+    assert mm(a, a, a, None, None, 8, 8, 128, None) == g.GPT2_EINVAL
+    assert mm(a, a + 4, a, a, None, 8, 8, 128, None) == g.GPT2_EINVAL
+    assert mm(a, a, a, a, a + 2, 8, 8, 128, None) == g.GPT2_EINVAL        # bias misaligned
+    assert mm(a, a, a, a, None, 8, 8, 100, None) == g.GPT2_ESHAPE         # K % 128
+    assert mm(a, a, a, a, None, 8, 12, 128, None) == g.GPT2_ESHAPE        # N % 8
+    assert mm(a, a, a, a, None, 0, 8, 128, None) == g.GPT2_ESHAPE
+    assert g.last_error()

@@ -226,7 +226,10 @@ struct GemmProblem {
     bf16* out2;            // EPI_BF16_GELU: gelu(out)
     const bf16* bias;      // EPI_BF16_B / BR / GELU: added per column
     const bf16* aux;       // EPI_BF16_R / BR: residual; EPI_BF16_DGELU: pre-activation
-    float* rowsum;         // or nullptr
+    union {
+        float* rowsum;         // or nullptr
+        const float* scales;   // EPI_FP8 / EPI_FP8_B: {s_x, s_w}
+    };
     int M, N, K;
 };
 struct GemmGroup {
@@ -274,7 +277,10 @@ void gemm_stream_kernel(const GemmGroup g) {
     using YO = LdsOperand<BN, BK, NW, YRC>;
     constexpr int SLOT = XO::ELEMS + YO::ELEMS;  // one ring slot: [X tile][Y tile]
     constexpr int LPS = XO::NPW + YO::NPW;       // load instructions per lane per stage
-    constexpr bool HAS_BIAS = EPI == EPI_BF16_B || EPI == EPI_BF16_BR || EPI == EPI_BF16_GELU;
+    constexpr bool FP8 = EPI == EPI_FP8 || EPI == EPI_FP8_B;
+    static_assert(!FP8 || (!XRC && !YRC), "E4M3 products: both operands reduction-contiguous");
+    constexpr bool HAS_BIAS =
+        EPI == EPI_BF16_B || EPI == EPI_BF16_BR || EPI == EPI_BF16_GELU || EPI == EPI_FP8_B;
     constexpr bool HAS_AUX = EPI == EPI_BF16_R || EPI == EPI_BF16_BR || EPI == EPI_BF16_DGELU;
     // buffer stores per lane per 32x32 output sub-tile, and per tile
     constexpr int SPT = EPI == EPI_F32 || EPI == EPI_BF16_GELU ? 4 : 2;
@@ -413,28 +419,61 @@ void gemm_stream_kernel(const GemmGroup g) {
                 }
             }
         }
-        bf16x8 a[2][FN], b[2][FM];
-        auto read_frags = [&](int kk, bf16x8* af, bf16x8* bfr) {
+        if constexpr (FP8) {
+            // E4M3: a slot row holds 2 BK codes; each 32x32x64 product takes
+            // 32 bytes per lane and operand: row r0 + l%32, slot chunks
+            // 4j + 2(l/32) and the one after (the same k order for both
+            // operands, which is all the product needs)
+            typedef int i32x8 __attribute__((ext_vector_type(8)));
+            auto frag8 = [&](const bf16* sb, int r0, int j) {
+                const int r = r0 + (lane & 31), c = 4 * j + 2 * (lane >> 5);
+                const u32x4 lo =
+                    *reinterpret_cast<const u32x4*>(sb + r * BK + ((c ^ pc_swz<BK>(r)) << 3));
+                const u32x4 hi = *reinterpret_cast<const u32x4*>(
+                    sb + r * BK + (((c + 1) ^ pc_swz<BK>(r)) << 3));
+                return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                             (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+            };
+            // one set of fragments at a time (32-byte fragments, double
+            // buffered, would not fit the register budget)
 #pragma unroll
-            for (int f = 0; f < FN; f++) af[f] = YO::frag(yb, wn * TN + f * 32, kk, lane);
+            for (int j = 0; j < BK / 32; j++) {
+                i32x8 a[FN], b[FM];
 #pragma unroll
-            for (int f = 0; f < FM; f++) bfr[f] = XO::frag(xb, wm * TM + f * 32, kk, lane);
-        };
-        read_frags(0, a[0], b[0]);
+                for (int f = 0; f < FN; f++) a[f] = frag8(yb, wn * TN + f * 32, j);
 #pragma unroll
-        for (int kk = 0; kk < BK / 16; kk++) {
-            // fragments of step kk+1 are requested before the products of
-            // step kk; the fences keep the compiler from sinking each read
-            // next to its first use
-            if (kk + 1 < BK / 16) read_frags(kk + 1, a[(kk + 1) & 1], b[(kk + 1) & 1]);
-            __builtin_amdgcn_sched_barrier(0);
+                for (int f = 0; f < FM; f++) b[f] = frag8(xb, wm * TM + f * 32, j);
 #pragma unroll
-            for (int fn = 0; fn < FN; fn++)
+                for (int fn = 0; fn < FN; fn++)
 #pragma unroll
-                for (int fm = 0; fm < FM; fm++)
-                    acc[fn][fm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        a[kk & 1][fn], b[kk & 1][fm], acc[fn][fm], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
+                    for (int fm = 0; fm < FM; fm++)
+                        acc[fn][fm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                            a[fn], b[fm], acc[fn][fm], 0, 0, 0, 0, 0, 0);
+            }
+        } else {
+            bf16x8 a[2][FN], b[2][FM];
+            auto read_frags = [&](int kk, bf16x8* af, bf16x8* bfr) {
+#pragma unroll
+                for (int f = 0; f < FN; f++) af[f] = YO::frag(yb, wn * TN + f * 32, kk, lane);
+#pragma unroll
+                for (int f = 0; f < FM; f++) bfr[f] = XO::frag(xb, wm * TM + f * 32, kk, lane);
+            };
+            read_frags(0, a[0], b[0]);
+#pragma unroll
+            for (int kk = 0; kk < BK / 16; kk++) {
+                // fragments of step kk+1 are requested before the products of
+                // step kk; the fences keep the compiler from sinking each read
+                // next to its first use
+                if (kk + 1 < BK / 16) read_frags(kk + 1, a[(kk + 1) & 1], b[(kk + 1) & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int fn = 0; fn < FN; fn++)
+#pragma unroll
+                    for (int fm = 0; fm < FM; fm++)
+                        acc[fn][fm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            a[kk & 1][fn], b[kk & 1][fm], acc[fn][fm], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
 
         if (++c_kt == c_nk) {
@@ -454,6 +493,7 @@ void gemm_stream_kernel(const GemmGroup g) {
                 for (int fm = 0; fm < FM; fm++) asm volatile("" : "+a"(acc[fn][fm]));
             const int M = pr.M, N = pr.N, ldo = N;
             const int i0 = c_tm * BM, j0 = c_tn * BN;
+            const float alpha = FP8 ? 1.f / (pr.scales[0] * pr.scales[1]) : 1.f;
             lds_barrier();  // every wave is done with slot_c
             float* sbase = reinterpret_cast<float*>(lds_ring + slot_c * SLOT);
             if constexpr (XRC) {
@@ -514,6 +554,9 @@ void gemm_stream_kernel(const GemmGroup g) {
                         const floatx4 lo = *reinterpret_cast<const floatx4*>(stage + r * SP + cl);
                         const floatx4 hi = *reinterpret_cast<const floatx4*>(stage + r * SP + cl + 4);
                         float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                        if constexpr (FP8)
+#pragma unroll
+                            for (int e = 0; e < 8; e++) v[e] *= alpha;
                         if constexpr (HAS_BIAS)
 #pragma unroll
                             for (int e = 0; e < 8; e++) v[e] += (float)biasv[fn & 1][e];

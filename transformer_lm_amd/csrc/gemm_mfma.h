@@ -99,7 +99,9 @@ struct Stager {
 // compile time: EPI_BF16_B: + bias; EPI_BF16_R: + residual; EPI_BF16_BR:
 // + bias + residual; EPI_BF16_GELU: out = bf16(acc + bias), out2 =
 // bf16(gelu(out)); EPI_BF16_DGELU: out = bf16(acc * gelu'(aux)) with aux the
-// bf16 pre-activation.
+// bf16 pre-activation. EPI_FP8 / EPI_FP8_B: both operands hold E4M3 codes
+// (two per bf16 slot, K counted in slots); out bf16 = acc / (s_x s_w)
+// (+ bias), with the two per-tensor scales read from device memory.
 enum {
     EPI_BF16 = 0,
     EPI_F32 = 1,
@@ -107,7 +109,9 @@ enum {
     EPI_BF16_DGELU = 3,
     EPI_BF16_B = 4,
     EPI_BF16_R = 5,
-    EPI_BF16_BR = 6
+    EPI_BF16_BR = 6,
+    EPI_FP8 = 7,
+    EPI_FP8_B = 8
 };
 
 // Tile coordinates of block `bid` of `total` = nbm x nbn tiles (see the file

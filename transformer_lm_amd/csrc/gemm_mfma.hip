@@ -46,6 +46,8 @@ static void prepare_lds_kernels() {
         (void)Lds::prepare<false, true, EPI_BF16_DGELU>();
         (void)Lds::prepare<true, true, EPI_F32>();
         (void)Lds::prepare<true, true, EPI_F32, false>();
+        (void)Lds::prepare<false, false, EPI_FP8>();
+        (void)Lds::prepare<false, false, EPI_FP8_B>();
     });
 }
 
@@ -199,5 +201,22 @@ bool gemm_bf16_bwd_dw_batch(const DwTask* tasks, int n, int M, hipStream_t st) {
         }
         Lds::run<true, true, EPI_F32, false>(g, st);  // builtin loads: measured faster here
     }
+    return true;
+}
+
+// out[M,N] (bf16) = (qx[M,K] . qw[N,K]^T) / (scales[0] scales[1]) (+ bias[N]),
+// qx and qw E4M3 codes; false (nothing launched) unless K is a multiple of
+// 128 codes (one tile depth) and N of 8.
+bool gemm_fp8_fwd(bf16* out, const uint8_t* qx, const uint8_t* qw, const float* scales,
+                  const bf16* bias, int M, int N, int K, hipStream_t st) {
+    if (K % (2 * LDS_BK) != 0 || N % 8 != 0) return false;
+    prepare_lds_kernels();
+    GemmProblem p{reinterpret_cast<const bf16*>(qx), reinterpret_cast<const bf16*>(qw), out,
+                  nullptr, bias, nullptr, nullptr, M, N, K / 2};
+    p.scales = scales;
+    if (bias)
+        Lds::run<false, false, EPI_FP8_B>(single(p), st);
+    else
+        Lds::run<false, false, EPI_FP8>(single(p), st);
     return true;
 }

@@ -831,4 +831,42 @@ void gpt2_free(gpt2* h) {
 
 const char* gpt2_last_error(void) { return g_err.c_str(); }
 
+// ---- FP8 (E4M3) products ------------------------------------------------------
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+int64_t gpt2_fp8_scale_workspace_bytes(void) { return fp8_scale_workspace_floats() * 4; }
+
+int gpt2_fp8_scale(float* scale, void* work, const void* x, int64_t n, void* hip_stream) {
+    if (!scale || !work || (!x && n > 0)) return fail(GPT2_EINVAL, "null pointer");
+    if (n < 0) return fail(GPT2_EINVAL, "negative size");
+    if (!aligned16(x) || ((uintptr_t)work & 255)) return fail(GPT2_EINVAL, "misaligned pointer");
+    fp8_scale(scale, (float*)work, (const bf16*)x, n, (hipStream_t)hip_stream);
+    return hip_status("gpt2_fp8_scale");
+}
+
+int gpt2_fp8_quantize(uint8_t* q, const void* x, const float* scale, int64_t n,
+                      void* hip_stream) {
+    if (!scale || ((!q || !x) && n > 0)) return fail(GPT2_EINVAL, "null pointer");
+    if (n < 0) return fail(GPT2_EINVAL, "negative size");
+    if (!aligned16(q) || !aligned16(x)) return fail(GPT2_EINVAL, "misaligned pointer");
+    if (n == 0) return GPT2_OK;
+    fp8_quantize(q, (const bf16*)x, scale, n, (hipStream_t)hip_stream);
+    return hip_status("gpt2_fp8_quantize");
+}
+
+int gpt2_fp8_matmul(void* out, const uint8_t* qx, const uint8_t* qw, const float* scales,
+                    const void* bias, int32_t M, int32_t N, int32_t K, void* hip_stream) {
+    if (!out || !qx || !qw || !scales) return fail(GPT2_EINVAL, "null pointer");
+    if (!aligned16(out) || !aligned16(qx) || !aligned16(qw) || !aligned16(bias))
+        return fail(GPT2_EINVAL, "misaligned pointer");
+    if (M <= 0 || N <= 0 || K <= 0) return fail(GPT2_ESHAPE, "M, N, K must be positive");
+    if (K % 128 != 0 || N % 8 != 0)
+        return fail(GPT2_ESHAPE, "K must be a multiple of 128 and N of 8");
+    if (!gemm_fp8_fwd((bf16*)out, qx, qw, scales, (const bf16*)bias, M, N, K,
+                      (hipStream_t)hip_stream))
+        return fail(GPT2_ESHAPE, "unsupported shape");
+    return hip_status("gpt2_fp8_matmul");
+}
+
 }  // extern "C"

@@ -153,3 +153,15 @@ void adamw(float* theta, const float* g, float* m, float* v, bf16* theta_bf16, i
 // out[0] = sqrt(sum g_i^2), deterministic; part: grad_norm_workspace_floats().
 int64_t grad_norm_workspace_floats();
 void grad_norm(float* out, float* part, const float* g, int64_t n, hipStream_t st);
+
+// ---- FP8 (E4M3) products ------------------------------------------------------
+// *scale = 448 / max|x_i| (1 for an all-zero x), deterministic; work:
+// fp8_scale_workspace_floats() floats. x 16-byte aligned.
+int64_t fp8_scale_workspace_floats();
+void fp8_scale(float* scale, float* work, const bf16* x, int64_t n, hipStream_t st);
+// q_i = E4M3(x_i * *scale), round to nearest even. q, x 16-byte aligned.
+void fp8_quantize(uint8_t* q, const bf16* x, const float* scale, int64_t n, hipStream_t st);
+// out[M,N] (bf16) = (qx[M,K] . qw[N,K]^T) / (scales[0] scales[1]) (+ bias[N]);
+// false (nothing launched) unless K % 128 == 0 and N % 8 == 0.
+bool gemm_fp8_fwd(bf16* out, const uint8_t* qx, const uint8_t* qw, const float* scales,
+                  const bf16* bias, int M, int N, int K, hipStream_t st);

@@ -29,7 +29,9 @@ EXPORTS = ("gpt2_num_params", "gpt2_num_param_tensors", "gpt2_param_table",
            "gpt2_backward", "gpt2_update", "gpt2_schedule_lr", "gpt2_update_scheduled",
            "gpt2_checkpoint_bytes", "gpt2_checkpoint_save", "gpt2_checkpoint_load",
            "gpt2_region", "gpt2_act", "gpt2_free",
-           "gpt2_last_error", "gpt2_timing_arm", "gpt2_timing_classes", "gpt2_timing_read")
+           "gpt2_last_error", "gpt2_timing_arm", "gpt2_timing_classes", "gpt2_timing_read",
+           "gpt2_fp8_scale_workspace_bytes", "gpt2_fp8_scale", "gpt2_fp8_quantize",
+           "gpt2_fp8_matmul")
 
 
 class Config(ct.Structure):
@@ -73,6 +75,11 @@ _SIG = {
     "gpt2_timing_read": (ct.c_int, [_P, ct.c_int, ct.POINTER(ct.c_char_p),
                                     ct.POINTER(ct.c_int64), ct.POINTER(ct.c_double),
                                     ct.POINTER(ct.c_double), ct.POINTER(ct.c_int32)]),
+    "gpt2_fp8_scale_workspace_bytes": (ct.c_int64, []),
+    "gpt2_fp8_scale": (ct.c_int, [_P, _P, _P, ct.c_int64, _P]),
+    "gpt2_fp8_quantize": (ct.c_int, [_P, _P, _P, ct.c_int64, _P]),
+    "gpt2_fp8_matmul": (ct.c_int, [_P, _P, _P, _P, _P, ct.c_int32, ct.c_int32, ct.c_int32,
+                                   _P]),
 }
 for _name, (_res, _args) in _SIG.items():
     _f = getattr(_lib, _name)
@@ -279,3 +286,40 @@ class GPT2:
             if n.value:
                 out[name.value.decode()] = (n.value, ms.value, wk.value, bool(isb.value))
         return out
+
+
+# ---- FP8 (E4M3) products: device tensors in, arguments marshalled only -------
+
+def _stream_of(t, stream):
+    import torch
+    return (stream if stream is not None else torch.cuda.current_stream(t.device)).cuda_stream
+
+
+def fp8_scale_workspace_bytes():
+    return int(_lib.gpt2_fp8_scale_workspace_bytes())
+
+
+def fp8_scale(scale, work, x, stream=None):
+    """scale[0] = 448 / max|x| (x bf16 on the device; scale a float32 device
+    tensor, work a uint8 device tensor of fp8_scale_workspace_bytes())."""
+    _check(_lib.gpt2_fp8_scale(scale.data_ptr(), work.data_ptr(), x.data_ptr(), x.numel(),
+                               _stream_of(x, stream)))
+
+
+def fp8_quantize(q, x, scale, stream=None):
+    """q = E4M3(x * scale[0]) (q a uint8 device tensor with x's element count)."""
+    if q.numel() != x.numel():
+        raise ValueError("q and x differ in size")
+    _check(_lib.gpt2_fp8_quantize(q.data_ptr(), x.data_ptr(), scale.data_ptr(), x.numel(),
+                                  _stream_of(x, stream)))
+
+
+def fp8_matmul(out, qx, qw, scales, bias=None, stream=None):
+    """out[M,N] (bf16) = (qx[M,K] . qw[N,K]^T) / (scales[0] scales[1]) (+ bias)."""
+    M, K = qx.shape
+    N = qw.shape[0]
+    if qw.shape[1] != K or tuple(out.shape) != (M, N):
+        raise ValueError("shape mismatch")
+    _check(_lib.gpt2_fp8_matmul(out.data_ptr(), qx.data_ptr(), qw.data_ptr(), scales.data_ptr(),
+                                None if bias is None else bias.data_ptr(), M, N, K,
+                                _stream_of(out, stream)))

@@ -16,6 +16,10 @@ LayerNorm gains 1, shifts 0; padded wte rows (>= V) are 0. The normal stream is
 indexed by flat position in the parameter array, so any slice can be
 regenerated on its own.
 
+FP8 product operands (fp8_operands): an activation block x[M, K] ~ N(0, 1)
+(the scale of LayerNorm outputs that feed the products), a weight w[N, K] ~
+N(0, 0.02) and a bias b[N] ~ N(0, 0.02), from three seeds derived from one.
+
 Tokens: uniform integers on [0, V) or a bounded Zipf law
 P(k) = (k+1)^-s / H over k in [0, V), drawn by inverse CDF on a float64
 cumulative table (smallest k with CDF(k) > u). Each optimiser step draws a
@@ -126,3 +130,14 @@ def split_batch(tok_step):
     """(B, T+1) block -> (inputs (B, T), targets (B, T)), both C-contiguous."""
     return (np.ascontiguousarray(tok_step[:, :-1]),
             np.ascontiguousarray(tok_step[:, 1:]))
+
+
+def fp8_operands(M, N, K, seed=20240):
+    """(x[M, K], w[N, K], b[N]) float32 for the FP8 products."""
+    x = np.empty(M * K, np.float32)
+    w = np.empty(N * K, np.float32)
+    b = np.empty(N, np.float32)
+    _fill_normal(x, seed, 0, 1.0)
+    _fill_normal(w, seed + 1, 0, 0.02)
+    _fill_normal(b, seed + 2, 0, 0.02)
+    return x.reshape(M, K), w.reshape(N, K), b
