@@ -7,7 +7,10 @@ Prints one JSON line: tokens/s, MFU against the bf16 dense peak, the dominant
 kernel class against its roofline (HIP-event durations measured in the timed
 steps), and the CPU oracle timed on a bounded sample of the same workload.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-fp8]
+
+A second object, "fp8_matmul", measures the FP8 (E4M3) products on the same
+model's forward shapes (not part of the training step, which stays bf16).
 """
 import argparse
 import json
@@ -21,6 +24,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_FLOPS = 2.5e15   # MI355X dense bf16 MFMA, published
+PEAK_FP8_FLOPS = 5.0e15    # MI355X dense fp8 MFMA, published
 PEAK_HBM_BYTES = 8.0e12    # MI355X HBM3E, published
 WORKLOAD = "gpt2_124m"
 
@@ -76,6 +80,69 @@ def cpu_baseline(w, T_sample=1024):
                       f"of {T_sample} tokens, fp64 oracle, {dt:.1f} s"}
 
 
+def fp8_leg(torch, gpt2, synth, M=16384, C=768, V=50304, reps=10):
+    """The FP8 (E4M3) products on the forward shapes of the 124M model at
+    M = B*T rows: per-tensor scale and quantisation of the operands, then the
+    product with a bf16 output, timed with events on the launch stream."""
+    shapes = {"qkv": (3 * C, C), "attproj": (C, C), "fc": (4 * C, C), "fcproj": (C, 4 * C),
+              "lm_head": (V, C)}
+    stream = torch.cuda.current_stream()
+    work = torch.empty(gpt2.fp8_scale_workspace_bytes(), dtype=torch.uint8, device="cuda")
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    per, tot_fl, tot_ms = {}, 0.0, 0.0
+    q_rate = s_rate = None
+    for name, (N, K) in shapes.items():
+        x, wt, b = synth.fp8_operands(M, N, K, seed=N + K)
+        xd = torch.from_numpy(x).cuda().to(torch.bfloat16)
+        wd = torch.from_numpy(wt).cuda().to(torch.bfloat16)
+        bd = torch.from_numpy(b).cuda().to(torch.bfloat16)
+        scales = torch.empty(4, dtype=torch.float32, device="cuda")
+        qx = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+        qw = torch.empty((N, K), dtype=torch.uint8, device="cuda")
+        gpt2.fp8_scale(scales[0:], work, xd)
+        gpt2.fp8_quantize(qx, xd, scales[0:])
+        gpt2.fp8_scale(scales[1:], work, wd)
+        gpt2.fp8_quantize(qw, wd, scales[1:])
+        out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        use_bias = name != "lm_head"
+        ms = timed(lambda: gpt2.fp8_matmul(out, qx, qw, scales, bd if use_bias else None))
+        fl = 2.0 * M * N * K
+        per[name] = {"N": N, "K": K, "ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 1)}
+        tot_fl += fl
+        tot_ms += ms
+        if name == "qkv":   # operand preparation, on the activation block [M, C]
+            ms_s = timed(lambda: gpt2.fp8_scale(scales[0:], work, xd))
+            ms_q = timed(lambda: gpt2.fp8_quantize(qx, xd, scales[0:]))
+            s_rate = 2.0 * xd.numel() / (ms_s * 1e-3) / 1e9
+            q_rate = 3.0 * xd.numel() / (ms_q * 1e-3) / 1e9
+        del xd, wd, bd, qx, qw, out
+    torch.cuda.empty_cache()
+    achieved = tot_fl / (tot_ms * 1e-3)
+    lm = per["lm_head"]
+    return {
+        "workload": f"E4M3 products of the 124M forward shapes at {M} rows (qkv, attproj, "
+                    f"fc, fcproj with bias; lm_head), per-tensor scales, bf16 output",
+        "per_shape": per,
+        "roofline": {"kernel": "fp8_matmul", "bound": "mfma",
+                     "achieved": round(achieved / 1e12, 1), "peak": PEAK_FP8_FLOPS / 1e12,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_FLOPS, 4),
+                     "lm_head_frac": round(lm["tflops"] * 1e12 / PEAK_FP8_FLOPS, 4)},
+        "scale_gb_s": round(s_rate, 1), "quantize_gb_s": round(q_rate, 1),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -83,6 +150,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default=WORKLOAD)
+    ap.add_argument("--no-fp8", action="store_true",
+                    help="skip the FP8 (E4M3) products' measurement")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run a plain 1 GiB device copy (reference for the "
                          "FETCH_SIZE / WRITE_SIZE counters)")
@@ -172,6 +241,15 @@ def main():
                     "traffic_fetch_write": [tr["fetch_bytes"], tr["write_bytes"]] if tr else None,
                     "launches": n, "avg_launch_ms": round(ms / n, 4)}
 
+    fp8 = None
+    if not args.no_fp8:
+        fp8 = fp8_leg(torch, gpt2, synth)
+        log("[bench] fp8 products: " + ", ".join(
+            f"{k} {v['tflops']:.0f}" for k, v in fp8["per_shape"].items()) +
+            f" TFLOP/s; all {fp8['roofline']['achieved']:.0f} TFLOP/s "
+            f"({100 * fp8['roofline']['frac']:.1f}% of fp8 peak); quantise "
+            f"{fp8['quantize_gb_s']:.0f} GB/s, scale {fp8['scale_gb_s']:.0f} GB/s")
+
     if args.calibrate_copy:
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
@@ -208,6 +286,7 @@ def main():
         "loss_first_last": [round(losses[0], 4), round(losses[-1], 4)] if losses else None,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "fp8_matmul": fp8,
     }
     print(json.dumps(out), flush=True)
 

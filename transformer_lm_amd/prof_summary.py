@@ -3,6 +3,7 @@
     python -m transformer_lm_amd.prof_summary stats  <kernel_stats.csv> [steps]
     python -m transformer_lm_amd.prof_summary traffic <fetch counter_collection.csv>
                                                       <write counter_collection.csv>
+    python -m transformer_lm_amd.prof_summary fp8 <kernel_trace.csv>
 
 `stats` prints each kernel's launches, total and average duration, and the
 launches grouped into the kernel classes the library's event timing reports.
@@ -17,6 +18,8 @@ from collections import defaultdict
 
 # kernel symbol (substring) -> library timing class
 CLASSES = [
+    (r"gemm_stream_kernel<[^>]*false, false, [78], ", "fp8_matmul"),
+    (r"fp8_", "fp8_prepare"),
     (r"gemm_(lds|mfma|persistent|stream)_kernel<[^>]*false, false", "matmul_fwd"),
     (r"gemm_(lds|mfma|persistent|stream)_kernel<[^>]*false, true", "matmul_bwd_dx"),
     (r"gemm_(lds|mfma|persistent|stream)_kernel<[^>]*true, true", "matmul_bwd_dw"),
@@ -146,9 +149,30 @@ def class_traffic(fetch_path, write_path, steps, L, copy_bytes=1 << 30):
     return {"fetch_scale": sf, "write_scale": sw, "classes": out}
 
 
+# the FP8 products bench.py times: per shape, 2 warmup + `reps` timed launches,
+# in this order (the lm-head without bias: its own kernel instantiation)
+FP8_SHAPES = ("qkv", "attproj", "fc", "fcproj", "lm_head")
+
+
+def fp8_products(trace_path, reps=10, warm=2):
+    """Average kernel-trace duration of each FP8 product's timed launches."""
+    rows = [r for r in csv.DictReader(open(trace_path))
+            if kclass(r["Kernel_Name"]) == "fp8_matmul"]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    per = len(rows) // len(FP8_SHAPES)
+    out = [f"{'product':10s} {'launches':>8s} {'avg us (timed)':>15s}"]
+    for i, name in enumerate(FP8_SHAPES):
+        grp = rows[i * per:(i + 1) * per][warm:warm + reps]
+        d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in grp]
+        out.append(f"{name:10s} {len(d):8d} {sum(d) / max(len(d), 1):15.2f}")
+    return "\n".join(out)
+
+
 if __name__ == "__main__":
     if sys.argv[1] == "stats":
         print(stats(sys.argv[2], int(sys.argv[3]) if len(sys.argv) > 3 else None))
+    elif sys.argv[1] == "fp8":
+        print(fp8_products(sys.argv[2]))
     elif sys.argv[1] == "traffic":
         print(traffic(sys.argv[2], sys.argv[3]))
     elif sys.argv[1] == "class-traffic":
