@@ -59,27 +59,37 @@ __device__ __forceinline__ int tswz(int r) { return (((r >> 1) & 1) << 2) | ((r 
 // small do not change a bf16 result).
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Buffer resource over the bytes at base; the launchers keep every offset of
-// one sequence's slice below 2^31.
+// Buffer resources over the bytes at base, for the builtin and the inline-asm
+// loads; the launchers keep every offset of one sequence's slice below 2^31.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t slice_rsrc(const void* base) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, 0x00020000);
 }
+__device__ __forceinline__ u32x4 slice_rsrc_asm(const void* base) { return raw_rsrc(base); }
 
-__device__ __forceinline__ __attribute__((address_space(3))) void* lds_ptr(const void* p) {
-    return (__attribute__((address_space(3))) void*)(p);
-}
-
-// Direct loads (buffer_load ... lds) of rows r0..r0+63 of a 64-wide head slice
-// (row stride ld elements, soff bytes past the resource base) into the LDS tile
-// s; rows >= nrows repeat row nrows-1. 4 waves, 2 loads each.
-__device__ __forceinline__ void dma_tile(bf16* s, __amdgpu_buffer_rsrc_t rs, int soff, int ld,
-                                         int r0, int nrows, int wid, int lane) {
+// Direct loads (buffer_load ... lds) of rows r0..r0+63 of a 64-wide head
+// slice (row stride ld elements, soff bytes past the resource base) into the
+// LDS tile s; rows >= nrows repeat row nrows-1. 4 waves, 2 loads each. ASM
+// issues them through inline asm (lds_dma16): the compiler then does not make
+// the current tile's transpose reads wait for the next tile's loads, and
+// tile_barrier's explicit wait is the one that covers them. Measured, the two
+// backward kernels gain from it and the forward kernel runs faster with the
+// builtin form.
+template <bool ASM, typename Rsrc>
+__device__ __forceinline__ void dma_tile(bf16* s, Rsrc rs, int soff, int ld, int r0, int nrows,
+                                         int wid, int lane) {
 #pragma unroll
     for (int j = 0; j < 2; j++) {
         const int blk = wid * 2 + j, ch = blk * 64 + lane;
         const int r = ch >> 3, lc = (ch & 7) ^ tswz(ch >> 3);
         const uint32_t off = (uint32_t)(min(r0 + r, nrows - 1) * ld + lc * 8) * 2u;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds_ptr(s + blk * 512), 16, off, soff, 0, 0);
+        if constexpr (ASM) {
+            lds_dma16(rs, off, (uint32_t)soff, s + blk * 512);
+        } else {
+#if __HIP_DEVICE_COMPILE__
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rs, (__attribute__((address_space(3))) void*)(s + blk * 512), 16, off, soff, 0, 0);
+#endif
+        }
     }
 }
 
@@ -137,8 +147,7 @@ __global__ __launch_bounds__(256, 4) void flash_fwd_kernel(bf16* __restrict__ ou
                                                         float* __restrict__ lse,
                                                         const bf16* __restrict__ qkv, int Tn,
                                                         int C, int NH) {
-    // the tile ring lives in dynamic LDS: the compiler does not then make
-    // reads of one buffer wait for the direct loads into the other
+    // the tile ring lives in dynamic LDS (four 8 KB tiles)
     extern __shared__ __attribute__((aligned(16))) bf16 ring[];
     auto Ks = [&](int i) { return ring + i * TILE_ELEMS; };
     auto Vs = [&](int i) { return ring + (2 + i) * TILE_ELEMS; };
@@ -161,14 +170,14 @@ __global__ __launch_bounds__(256, 4) void flash_fwd_kernel(bf16* __restrict__ ou
     float m = -INFINITY, l = 0.f;
 
     const int ntiles = (min(Tn, (qt + 1) * Q_PER_BLOCK) + TILE - 1) / TILE;
-    dma_tile(Ks(0), rs, 2 * C, C3, 0, Tn, wid, lane);
-    dma_tile(Vs(0), rs, 4 * C, C3, 0, Tn, wid, lane);
+    dma_tile<false>(Ks(0), rs, 2 * C, C3, 0, Tn, wid, lane);
+    dma_tile<false>(Vs(0), rs, 4 * C, C3, 0, Tn, wid, lane);
     for (int t = 0; t < ntiles; t++) {
         const int buf = t & 1, k0 = t * TILE;
         tile_barrier();
         if (t + 1 < ntiles) {
-            dma_tile(Ks(buf ^ 1), rs, 2 * C, C3, k0 + TILE, Tn, wid, lane);
-            dma_tile(Vs(buf ^ 1), rs, 4 * C, C3, k0 + TILE, Tn, wid, lane);
+            dma_tile<false>(Ks(buf ^ 1), rs, 2 * C, C3, k0 + TILE, Tn, wid, lane);
+            dma_tile<false>(Vs(buf ^ 1), rs, 4 * C, C3, k0 + TILE, Tn, wid, lane);
         }
         if (k0 > q0 + 31 || q0 >= Tn) continue;  // every key of the tile is masked
         const bf16* kt_s = Ks(buf);
@@ -259,9 +268,9 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkv_kernel(
     const int C3 = 3 * C;
     const bf16* base = qkv + (int64_t)b * Tn * C3 + h * HS;
     const bf16* dbase = dout + (int64_t)b * Tn * C + h * HS;
-    const auto rq = slice_rsrc(base);
-    const auto ro = slice_rsrc(dbase);
-    const auto rl = slice_rsrc(wid == 2 ? lse + (int64_t)bh * Tn : Dbuf + (int64_t)bh * Tn);
+    const auto rq = slice_rsrc_asm(base);
+    const auto ro = slice_rsrc_asm(dbase);
+    const auto rl = slice_rsrc_asm(wid == 2 ? lse + (int64_t)bh * Tn : Dbuf + (int64_t)bh * Tn);
     const int kb0 = kq * Q_PER_BLOCK;
     const int kw = kb0 + wid * 32;
     const int kl = kw + (lane & 31);
@@ -279,12 +288,11 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkv_kernel(
     // by direct loads (wave 2: log-sum-exp, wave 3: D), one float a lane
     auto issue = [&](int t, int buf) {
         const int q0 = kb0 + t * TILE;
-        dma_tile(Qs(buf), rq, 0, C3, q0, Tn, wid, lane);
-        dma_tile(Os(buf), ro, 0, C, q0, Tn, wid, lane);
+        dma_tile<true>(Qs(buf), rq, 0, C3, q0, Tn, wid, lane);
+        dma_tile<true>(Os(buf), ro, 0, C, q0, Tn, wid, lane);
         if (wid >= 2) {
             const uint32_t off = (uint32_t)min(q0 + lane, Tn - 1) * 4u;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, lds_ptr(wid == 2 ? ls(buf) : Ds(buf)), 4,
-                                                     off, 0, 0, 0);
+            lds_dma4(rl, off, 0, wid == 2 ? ls(buf) : Ds(buf));
         }
     };
     const int ntiles = (Tn - kb0 + TILE - 1) / TILE;
@@ -377,7 +385,7 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(
     const int b = bh / NH, h = bh % NH;
     const int C3 = 3 * C;
     const bf16* base = qkv + (int64_t)b * Tn * C3 + h * HS;
-    const auto rs = slice_rsrc(base);
+    const auto rs = slice_rsrc_asm(base);
     const int q0 = qt * Q_PER_BLOCK + wid * 32;
     const int ql = q0 + (lane & 31);
     const float sc = LOG2E / 8.0f;
@@ -411,14 +419,14 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(
     floatx16 dq[2] = {floatx16{}, floatx16{}};
 
     const int ntiles = (min(Tn, (qt + 1) * Q_PER_BLOCK) + TILE - 1) / TILE;
-    dma_tile(Ks(0), rs, 2 * C, C3, 0, Tn, wid, lane);
-    dma_tile(Vs(0), rs, 4 * C, C3, 0, Tn, wid, lane);
+    dma_tile<true>(Ks(0), rs, 2 * C, C3, 0, Tn, wid, lane);
+    dma_tile<true>(Vs(0), rs, 4 * C, C3, 0, Tn, wid, lane);
     for (int t = 0; t < ntiles; t++) {
         const int buf = t & 1, k0 = t * TILE;
         tile_barrier();
         if (t + 1 < ntiles) {
-            dma_tile(Ks(buf ^ 1), rs, 2 * C, C3, k0 + TILE, Tn, wid, lane);
-            dma_tile(Vs(buf ^ 1), rs, 4 * C, C3, k0 + TILE, Tn, wid, lane);
+            dma_tile<true>(Ks(buf ^ 1), rs, 2 * C, C3, k0 + TILE, Tn, wid, lane);
+            dma_tile<true>(Vs(buf ^ 1), rs, 4 * C, C3, k0 + TILE, Tn, wid, lane);
         }
         if (k0 > q0 + 31 || q0 >= Tn) continue;
         const bf16* ks = Ks(buf);
