@@ -14,7 +14,8 @@ __device__ __forceinline__ void adamw_one(float& th, float g, float& m, float& v
     th -= lr * (mhat / (sqrtf(vhat) + eps) + wd * th);
 }
 
-// Each thread handles two float4 groups per iteration (8 loads in flight);
+#define ADAMW_GROUPS 4
+// Each thread handles ADAMW_GROUPS float4 groups per iteration (16 loads in flight);
 // the streams are touched once, so loads and stores bypass cache retention.
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ f32x4 ld_nt(const float* p) {
@@ -41,39 +42,43 @@ __global__ __launch_bounds__(256) void adamw_kernel(float* __restrict__ theta,
                                                     const float* __restrict__ gnorm, float clip) {
     typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
     const float gs = clip_scale(gnorm, clip);
-    const int64_t n8 = n / 8;
+    constexpr int U = ADAMW_GROUPS;
+    const int64_t nq = n / (4 * U);  // groups of 4 per stream
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n8; i += stride) {
-        const int64_t e0 = i * 4, e1 = (i + n8) * 4;  // two groups n/2 apart: both streams coalesce
-        f32x4 th[2] = {ld_nt(theta + e0), ld_nt(theta + e1)};
-        const f32x4 gg[2] = {ld_nt(g + e0) * gs, ld_nt(g + e1) * gs};
-        f32x4 mm[2] = {ld_nt(m + e0), ld_nt(m + e1)};
-        f32x4 vv[2] = {ld_nt(v + e0), ld_nt(v + e1)};
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < nq; i += stride) {
+        // U groups nq*4 elements apart: every stream coalesces
+        int64_t e[U];
+        f32x4 th[U], gg[U], mm[U], vv[U];
 #pragma unroll
-        for (int u = 0; u < 2; u++)
+        for (int u = 0; u < U; u++) {
+            e[u] = (i + u * nq) * 4;
+            th[u] = ld_nt(theta + e[u]);
+            gg[u] = ld_nt(g + e[u]) * gs;
+            mm[u] = ld_nt(m + e[u]);
+            vv[u] = ld_nt(v + e[u]);
+        }
 #pragma unroll
-            for (int e = 0; e < 4; e++) {
-                float t = th[u][e], a = mm[u][e], b = vv[u][e];
-                adamw_one(t, gg[u][e], a, b, lr, b1, b2, eps, wd, c1, c2);
-                th[u][e] = t;
-                mm[u][e] = a;
-                vv[u][e] = b;
+        for (int u = 0; u < U; u++)
+#pragma unroll
+            for (int k = 0; k < 4; k++) {
+                float t = th[u][k], a = mm[u][k], b = vv[u][k];
+                adamw_one(t, gg[u][k], a, b, lr, b1, b2, eps, wd, c1, c2);
+                th[u][k] = t;
+                mm[u][k] = a;
+                vv[u][k] = b;
             }
-        st_nt(theta + e0, th[0]);
-        st_nt(theta + e1, th[1]);
-        st_nt(m + e0, mm[0]);
-        st_nt(m + e1, mm[1]);
-        st_nt(v + e0, vv[0]);
-        st_nt(v + e1, vv[1]);
-        if (theta_bf16) {
-            *reinterpret_cast<bf16x4*>(theta_bf16 + e0) =
-                bf16x4{(bf16)th[0][0], (bf16)th[0][1], (bf16)th[0][2], (bf16)th[0][3]};
-            *reinterpret_cast<bf16x4*>(theta_bf16 + e1) =
-                bf16x4{(bf16)th[1][0], (bf16)th[1][1], (bf16)th[1][2], (bf16)th[1][3]};
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            st_nt(theta + e[u], th[u]);
+            st_nt(m + e[u], mm[u]);
+            st_nt(v + e[u], vv[u]);
+            if (theta_bf16)
+                *reinterpret_cast<bf16x4*>(theta_bf16 + e[u]) =
+                    bf16x4{(bf16)th[u][0], (bf16)th[u][1], (bf16)th[u][2], (bf16)th[u][3]};
         }
     }
-    // tail (n % 8 elements)
-    for (int64_t i = n8 * 8 + blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += stride) {
+    // tail (n % (4U) elements)
+    for (int64_t i = nq * 4 * U + blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += stride) {
         float th = theta[i], mm = m[i], vv = v[i];
         adamw_one(th, g[i] * gs, mm, vv, lr, b1, b2, eps, wd, c1, c2);
         theta[i] = th;
@@ -86,7 +91,7 @@ __global__ __launch_bounds__(256) void adamw_kernel(float* __restrict__ theta,
 void adamw(float* theta, const float* g, float* m, float* v, bf16* theta_bf16, int64_t n,
            float lr, float b1, float b2, float eps, float wd, float c1, float c2,
            const float* gnorm, float clip, hipStream_t st) {
-    int64_t blocks = (n / 8 + 255) / 256;
+    int64_t blocks = (n / (4 * ADAMW_GROUPS) + 255) / 256;
     if (blocks > 8192) blocks = 8192;
     if (blocks < 1) blocks = 1;
     adamw_kernel<<<(int)blocks, 256, 0, st>>>(theta, g, m, v, theta_bf16, n, lr, b1, b2, eps, wd,
