@@ -229,6 +229,11 @@ def _bf16_cases():
         ("gpt2_124m_B2T96", WORKLOADS["gpt2_124m"].with_batch(B=2, T=96, steps=2)),
         ("gpt2_350m_L2_B1T128", replace(WORKLOADS["gpt2_350m"], L=2, B=1, T=128, steps=2)),
         ("gpt2_1558m_L2_B1T64", replace(WORKLOADS["gpt2_1558m"], L=2, B=1, T=64, steps=2)),
+        # degenerate and ragged: one-token sequences (attention over a single
+        # key, 3 GEMM rows), and B*T = 130 (not a multiple of the 64-row
+        # reduction depth: the weight gradients take the register-staged path)
+        ("gpt2_124m_L2_B3T1", replace(WORKLOADS["gpt2_124m"], L=2, B=3, T=1, steps=2)),
+        ("gpt2_124m_L2_B1T130", replace(WORKLOADS["gpt2_124m"], L=2, B=1, T=130, steps=2)),
     ]
 
 
