@@ -5,12 +5,12 @@
 // the softmax and get a zero gradient.
 #include "kernels.h"
 
-#define CL_THREADS 512
+#define CL_THREADS 1024
 
 // One block per row: pass 1 keeps a per-thread running (max, sum of exp)
 // over 8-column chunks, merged across the block; pass 2 writes
 // dz = (exp(z - lse) - [v == target]) * dloss. Used for vocabularies too wide
-// for the register-resident kernel below (more than 13 * 4096 columns).
+// for the register-resident kernel below (more than 7 * 8192 columns).
 template <typename T>
 __global__ __launch_bounds__(CL_THREADS) void classifier_kernel(T* logits,
                                                                 float* __restrict__ losses,
@@ -62,7 +62,9 @@ __global__ __launch_bounds__(CL_THREADS) void classifier_kernel(T* logits,
     }
 }
 
-// Single HBM pass: each thread keeps its NCHK chunks of 8 logits in registers
+// Single HBM pass, one 1024-thread block per row (a 50304-column row is 7
+// chunks per thread, 56 registers: two rows per CU at 8 waves per SIMD): each
+// thread keeps its NCHK chunks of 8 logits in registers
 // (the row is read once), runs the online (max, sum of exp) over them, and
 // after the block-wide merge writes the gradients from the same registers.
 // exp(x) is evaluated as 2^(x log2 e) on the hardware exponential.
@@ -106,7 +108,7 @@ __device__ __forceinline__ void store8_nt(T* p, const float (&v)[8]) {
 // a path without per-column tests; the chunk holding the target also yields
 // the target's logit from registers, and its lane writes the row's loss.
 template <typename T, int NCHK>
-__global__ __launch_bounds__(CL_THREADS) __attribute__((amdgpu_waves_per_eu(4))) void classifier_reg_kernel(
+__global__ __launch_bounds__(CL_THREADS) void classifier_reg_kernel(
     T* logits, float* __restrict__ losses, const int32_t* __restrict__ targets, int V, int Vp,
     float dloss, int* err) {
     __shared__ float red[16];
@@ -199,8 +201,8 @@ void classifier_fwd(T* logits, float* losses, const int32_t* targets, int N, int
         classifier_reg_kernel<T, 1><<<N, CL_THREADS, 0, st>>>(logits, losses, targets, V, Vp, dloss, err);
     else if (nchk <= 4)
         classifier_reg_kernel<T, 4><<<N, CL_THREADS, 0, st>>>(logits, losses, targets, V, Vp, dloss, err);
-    else if (nchk <= 13)
-        classifier_reg_kernel<T, 13><<<N, CL_THREADS, 0, st>>>(logits, losses, targets, V, Vp, dloss, err);
+    else if (nchk <= 7)
+        classifier_reg_kernel<T, 7><<<N, CL_THREADS, 0, st>>>(logits, losses, targets, V, Vp, dloss, err);
     else
         classifier_kernel<T><<<N, CL_THREADS, 0, st>>>(logits, losses, targets, V, Vp, dloss, err);
 }
