@@ -68,7 +68,7 @@ __global__ __launch_bounds__(256) void encoder_bwd_wpe_kernel(float* __restrict_
 // summed in a fixed order, so the result does not depend on scheduling.
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-#define ENC_CHUNK 1024
+#define ENC_CHUNK 256
 #define ENC_SCAN 4096  // elements per scan block (1024 threads x 4)
 #define ENC_RANGE 32
 
@@ -112,7 +112,7 @@ int64_t encoder_bwd_workspace_bytes(int BT, int Vp, int C) {
 
 // One block per chunk: ranks inside the chunk and the chunk's token counts
 // (written by the last position of each token in the chunk).
-__global__ __launch_bounds__(1024) void enc_rank_kernel(const int32_t* __restrict__ tok, int BT,
+__global__ __launch_bounds__(ENC_CHUNK) void enc_rank_kernel(const int32_t* __restrict__ tok, int BT,
                                                         int Vp, int nch, int* __restrict__ count,
                                                         int* __restrict__ rank) {
     __shared__ int sh[ENC_CHUNK];
@@ -338,7 +338,7 @@ void encoder_bwd(float* dwte, float* dwpe, const T* dout, const int32_t* tok, in
     const EncWs w = enc_ws(ws, BT, Vp, C);
     const int64_t ncount = (int64_t)Vp * w.nch;
     fill_zero_i32(w.scan, ncount, st);
-    enc_rank_kernel<<<w.nch, 1024, 0, st>>>(tok, BT, Vp, w.nch, w.scan, w.rank);
+    enc_rank_kernel<<<w.nch, ENC_CHUNK, 0, st>>>(tok, BT, Vp, w.nch, w.scan, w.rank);
     enc_scan_block_kernel<<<w.nsb, 1024, 0, st>>>(w.scan, ncount, w.bsum);
     enc_scan_totals_kernel<<<1, 1024, 0, st>>>(w.bsum, w.nsb);
     enc_fill_kernel<<<ceil_div(BT, 256), 256, 0, st>>>(tok, BT, Vp, w.nch, w.nsb, w.scan, w.bsum,
