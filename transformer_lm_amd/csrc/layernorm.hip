@@ -140,7 +140,7 @@ void layernorm_fwd(T* out, float* mean, float* rstd, const T* inp, const T* w, c
 // each lane sums its channels over its rows in row order, the four waves are
 // combined in wave order through LDS into one partial row per block, and a
 // second kernel sums the partial rows in a fixed order.
-#define LN_BWD_BLOCKS 1024
+#define LN_BWD_BLOCKS 512
 #define LN_BWD_RPW 2
 static_assert(4 * LN_BWD_RPW == LN_BWD_ROWS, "four waves of LN_BWD_RPW rows per pass");
 
