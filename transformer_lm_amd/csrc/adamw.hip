@@ -92,7 +92,7 @@ void adamw(float* theta, const float* g, float* m, float* v, bf16* theta_bf16, i
            float lr, float b1, float b2, float eps, float wd, float c1, float c2,
            const float* gnorm, float clip, hipStream_t st) {
     int64_t blocks = (n / (4 * ADAMW_GROUPS) + 255) / 256;
-    if (blocks > 8192) blocks = 8192;
+    if (blocks > 65536) blocks = 65536;  // one pass per thread up to 2^28 parameters
     if (blocks < 1) blocks = 1;
     adamw_kernel<<<(int)blocks, 256, 0, st>>>(theta, g, m, v, theta_bf16, n, lr, b1, b2, eps, wd,
                                               c1, c2, gnorm, clip);
