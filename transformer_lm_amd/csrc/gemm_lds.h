@@ -169,10 +169,14 @@ struct LdsOperand {
 // next tile's first stages load while the current tile finishes and while its
 // epilogue drains.
 #define GROUP_MAX 52  // the 4 weight gradients of 12 layers and the tied output head
-// Cache policy of the epilogue's buffer stores: non-temporal (nt), so the
-// written outputs do not displace the operand panels that the L2 serves to
-// the other tiles.
+// Cache policy of the epilogue's buffer stores. Non-temporal (nt) keeps the
+// written outputs from displacing the operand panels that the L2 serves to
+// the other tiles; measured in the training step, it pays for the forward
+// products and the weight gradients. The input-gradient products (dX layout)
+// store with the default policy: the next kernels read those gradients while
+// they are still cached (step time -0.8%).
 #define ST_NT 2
+#define ST_POLICY(EPI, XRC, YRC, FP8) ((!(XRC) && (YRC)) ? 0 : ST_NT)
 struct GemmProblem {
     const bf16* X;
     const bf16* Y;
@@ -232,6 +236,7 @@ void gemm_stream_kernel(const GemmGroup g) {
     constexpr int SLOT = XO::ELEMS + YO::ELEMS;  // one ring slot: [X tile][Y tile]
     constexpr int LPS = XO::NPW + YO::NPW;       // load instructions per lane per stage
     constexpr bool FP8 = EPI == EPI_FP8 || EPI == EPI_FP8_B;
+    constexpr int ST_POL = ST_POLICY(EPI, XRC, YRC, FP8);
     static_assert(!FP8 || (!XRC && !YRC), "E4M3 products: both operands reduction-contiguous");
     constexpr bool HAS_BIAS =
         EPI == EPI_BF16_B || EPI == EPI_BF16_BR || EPI == EPI_BF16_GELU || EPI == EPI_FP8_B;
@@ -498,7 +503,7 @@ void gemm_stream_kernel(const GemmGroup g) {
                             j < N ? (uint32_t)(((fm * 32 + r) * ldo + j) * 4) : 0x80000000u;
                         const floatx4 v = *reinterpret_cast<const floatx4*>(stage + r * SP + c);
                         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs_out,
-                                                               off, 0, ST_NT);
+                                                               off, 0, ST_POL);
                     }
                 } else {
 #pragma unroll
@@ -527,13 +532,13 @@ void gemm_stream_kernel(const GemmGroup g) {
                         const uint32_t off =
                             j < N ? (uint32_t)(((fm * 32 + r) * ldo + j) * 2) : 0x80000000u;
                         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), rs_out,
-                                                               off, 0, ST_NT);
+                                                               off, 0, ST_POL);
                         if constexpr (EPI == EPI_BF16_GELU) {
                             bf16x8 ga;
 #pragma unroll
                             for (int e = 0; e < 8; e++) ga[e] = (bf16)gelu_fast((float)o[e]);
                             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ga),
-                                                                   rs_out2, off, 0, ST_NT);
+                                                                   rs_out2, off, 0, ST_POL);
                         }
                     }
                 }
