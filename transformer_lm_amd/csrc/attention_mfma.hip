@@ -26,10 +26,10 @@
 //
 // Softmax runs in base 2: x = s * log2(e) / sqrt(hs), p = exp2(x - m).
 //
-// Launch bounds ask for 4 (forward), 2 (dK/dV) and 3 (dQ) waves per SIMD:
-// the register budgets that fit keep every kernel free of spills, and the
-// extra waves hide the matrix-core / exponential / LDS latencies of each
-// wave's serial tile loop.
+// Launch bounds ask for 4 (forward) and 2 (dK/dV, dQ) waves per SIMD: the
+// register budgets that fit keep every kernel free of spills (dQ needs under
+// 170 registers and so runs 3 waves per SIMD), and the extra waves hide the
+// matrix-core / exponential / LDS latencies of each wave's serial tile loop.
 #include <type_traits>
 
 #include "gemm_lds.h"
@@ -40,6 +40,11 @@
 #define TILE_ELEMS (TILE * HS)
 #define LOG2E 1.4426950408889634f
 #define LN2 0.6931471805599453f
+// The forward pass keeps its running reference maximum until a tile's maximum
+// exceeds it by more than this (base 2), so probabilities stay below 2^8 and
+// most tiles skip rescaling the output accumulators. O / l and the
+// log-sum-exp m + log2(l) do not depend on which reference is used.
+#define RESCALE_SLACK 8.0f
 
 __device__ __forceinline__ floatx16 mfma(bf16x8 a, bf16x8 b, floatx16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -111,6 +116,38 @@ __device__ __forceinline__ bf16x8 frag_dims(const bf16* s, int d0, int base, int
     const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)pb);
     const v4i16 v[2] = {lo, hi};
     return *reinterpret_cast<const bf16x8*>(v);
+}
+
+// Lanes l and l ^ 32 combined: the swap of the upper half of one copy of x
+// with the lower half of another leaves every lane holding x of lane l % 32 in
+// one register and x of lane l % 32 + 32 in the other, so both lanes of a pair
+// combine the same two values in the same order (no LDS round trip).
+__device__ __forceinline__ void half_pair(float x, float& lo, float& hi) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    lo = __uint_as_float(r[0]);
+    hi = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float half_pair_max(float x) {
+    float lo, hi;
+    half_pair(x, lo, hi);
+    return fmaxf(lo, hi);
+}
+__device__ __forceinline__ float half_pair_sum(float x) {
+    float lo, hi;
+    half_pair(x, lo, hi);
+    return lo + hi;
+}
+
+// acc + the sum of the 8 bf16 values, exact products by one on the dot unit
+// (four v_dot2_f32_bf16, accumulating in fp32).
+__device__ __forceinline__ float sum_bf16x8(const bf16x8& v, float acc) {
+    typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 one = {(bf16)1.f, (bf16)1.f};
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+        acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{v[2 * i], v[2 * i + 1]}, one, acc, false);
+    return acc;
 }
 
 // Registers 8*hh .. 8*hh+7 of an accumulator, rounded to bf16.
@@ -201,34 +238,36 @@ __global__ __launch_bounds__(256, 4) void flash_fwd_kernel(bf16* __restrict__ ou
         for (int kt = 0; kt < 2; kt++)
 #pragma unroll
             for (int v = 0; v < 16; v++) mx = fmaxf(mx, s[kt][v]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        // every processed tile holds a visible key for every lane, so mn is finite
-        const float mn = fmaxf(m, mx * sc);
-        const float corr = exp2_fast(m - mn);
-        float ps = 0.f;
+        mx = half_pair_max(mx);
+        // every processed tile holds a visible key for every lane, so mt is
+        // finite; the reference m moves only when the tile's maximum passes it
+        // by more than RESCALE_SLACK (always on a lane's first tile)
+        const float mt = mx * sc;
+        const bool up = mt > m + RESCALE_SLACK;
+        if (__builtin_amdgcn_ballot_w64(up)) {  // wave-uniform
+            const float mn = up ? mt : m;
+            const float corr = exp2_fast(m - mn);
+            l *= corr;
+            o[0] *= corr;
+            o[1] *= corr;
+            m = mn;
+        }
 #pragma unroll
         for (int kt = 0; kt < 2; kt++)
 #pragma unroll
-            for (int v = 0; v < 16; v++) {
-                const float p = exp2_fast(fmaf(s[kt][v], sc, -mn));
-                s[kt][v] = p;
-                ps += p;
-            }
-        ps += __shfl_xor(ps, 32, 64);
-        l = l * corr + ps;
-        m = mn;
-        o[0] *= corr;
-        o[1] *= corr;
+            for (int v = 0; v < 16; v++) s[kt][v] = exp2_fast(fmaf(s[kt][v], sc, -m));
 #pragma unroll
         for (int kt = 0; kt < 2; kt++)
 #pragma unroll
             for (int hh = 0; hh < 2; hh++) {
                 const bf16x8 pb = half_tile(s[kt], hh);
+                l = sum_bf16x8(pb, l);
 #pragma unroll
                 for (int dt = 0; dt < 2; dt++)
                     o[dt] = mfma(frag_dims(vt_s, 32 * dt, 32 * kt + 16 * hh, lane), pb, o[dt]);
             }
     }
+    l = half_pair_sum(l);  // each half summed its own keys
     if (ql < Tn) {
         const float inv = 1.f / l;
         bf16* orow = out + ((int64_t)b * Tn + ql) * C + h * HS;
