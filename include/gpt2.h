@@ -250,6 +250,29 @@ int gpt2_fp8_quantize(uint8_t* q, const void* x, const float* scale, int64_t n,
 int gpt2_fp8_matmul(void* out, const uint8_t* qx, const uint8_t* qw, const float* scales,
                     const void* bias, int32_t M, int32_t N, int32_t K, void* hip_stream);
 
+/* ---- causal self-attention on its own ----------------------------------
+ * The attention step of every block (page "llm.c: Large Language Model
+ * Training in Pure C/CUDA Without Dependencies", section "Fused Attention
+ * Kernel"; page "Building GPT-2 from scratch", exercise table row A1), the
+ * same kernels gpt2_forward runs, on caller-owned device buffers and without
+ * a handle:
+ *   qkv  (B, T, 3C) row-major, dtype-typed: per token the C query, C key and
+ *        C value channels, head h owning channels h*hs .. h*hs+hs-1 of each
+ *        (hs = C / NH);
+ *   out  (B, T, C) row-major, dtype-typed: out[b,t,h*hs+d] = sum over t' <= t
+ *        of softmax_t'(q_t . k_t' / sqrt(hs)) v_t'[d];
+ *   lse  (B, NH, T) fp32: the natural-log log-sum-exp of each query's scaled
+ *        scores (what the backward pass rebuilds the probabilities from).
+ * bf16 with hs = 64 runs on the matrix cores; other head sizes and fp32 on the
+ * row kernels. Asynchronous on hip_stream (a hipStream_t, NULL: the null
+ * stream). Pointers 16-byte aligned. Returns GPT2_OK, GPT2_EINVAL (null or
+ * misaligned pointer, bad dtype), GPT2_ESHAPE (need C % 8 == 0, C <= 2048,
+ * hs a multiple of 8 and at most 128, B*T <= 524288, B*NH <= 65535) or
+ * GPT2_EHIP (launch failed).
+ */
+int gpt2_attention_forward(void* out, float* lse, const void* qkv, int32_t B, int32_t T,
+                           int32_t C, int32_t NH, int32_t dtype, void* hip_stream);
+
 /* Message for the most recent failure on this thread ("" if none). */
 const char* gpt2_last_error(void);
 

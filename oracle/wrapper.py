@@ -279,3 +279,20 @@ def fp8_matmul(qx, qw, sx, sw, bias=None):
     lib.oracle_fp8_matmul(ptr(out, ct.c_double), ptr(qx, ct.c_ubyte), ptr(qw, ct.c_ubyte),
                           ptr(b, ct.c_double), M, N, K, float(sx), float(sw))
     return out
+
+
+# ---- causal attention on its own ---------------------------------------------
+
+def attention_forward(qkv, NH):
+    """The oracle's causal attention of fused (B, T, 3C) activations: out
+    (B, T, C) and the probabilities att (B, NH, T, T), float64."""
+    lib = load()
+    qkv = np.ascontiguousarray(qkv, np.float64)
+    B, T, C3 = qkv.shape
+    C = C3 // 3
+    assert C3 == 3 * C and C % NH == 0
+    out = np.empty((B, T, C), np.float64)
+    att = np.empty((B, NH, T, T), np.float64)
+    lib.oracle_attention_forward(ptr(out, ct.c_double), ptr(att, ct.c_double),
+                                 ptr(qkv, ct.c_double), B, T, C, NH)
+    return out, att

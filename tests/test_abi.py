@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(g):
     names = declared_functions()
-    assert len(names) == 25
+    assert len(names) == 26
     lib = ct.CDLL(g.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -117,4 +117,21 @@ def test_fp8_entry_points_validate_before_launching(g):
     assert mm(a, a, a, a, None, 8, 8, 100, None) == g.GPT2_ESHAPE         # K % 128
     assert mm(a, a, a, a, None, 8, 12, 128, None) == g.GPT2_ESHAPE        # N % 8
     assert mm(a, a, a, a, None, 0, 8, 128, None) == g.GPT2_ESHAPE
+    assert g.last_error()
+
+
+def test_attention_entry_point_validates_before_launching(g):
+    att = g._lib.gpt2_attention_forward
+    a = 1 << 20                                      # 16-byte aligned, never dereferenced
+    bf16 = g.DTYPE_BF16
+    assert att(None, a, a, 1, 8, 128, 2, bf16, None) == g.GPT2_EINVAL
+    assert att(a, None, a, 1, 8, 128, 2, bf16, None) == g.GPT2_EINVAL
+    assert att(a, a, a + 2, 1, 8, 128, 2, bf16, None) == g.GPT2_EINVAL     # qkv misaligned
+    assert att(a, a, a, 1, 8, 128, 2, 7, None) == g.GPT2_EINVAL            # dtype
+    assert att(a, a, a, 0, 8, 128, 2, bf16, None) == g.GPT2_ESHAPE
+    assert att(a, a, a, 1, 0, 128, 2, bf16, None) == g.GPT2_ESHAPE
+    assert att(a, a, a, 1, 8, 120, 2, bf16, None) == g.GPT2_ESHAPE         # head size 60
+    assert att(a, a, a, 1, 8, 512, 2, bf16, None) == g.GPT2_ESHAPE         # head size 256
+    assert att(a, a, a, 1, 8, 128, 3, bf16, None) == g.GPT2_ESHAPE         # C % NH
+    assert att(a, a, a, 1024, 1024, 128, 2, bf16, None) == g.GPT2_ESHAPE   # B*T
     assert g.last_error()

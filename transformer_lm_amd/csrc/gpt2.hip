@@ -869,4 +869,25 @@ int gpt2_fp8_matmul(void* out, const uint8_t* qx, const uint8_t* qw, const float
     return hip_status("gpt2_fp8_matmul");
 }
 
+int gpt2_attention_forward(void* out, float* lse, const void* qkv, int32_t B, int32_t T,
+                           int32_t C, int32_t NH, int32_t dtype, void* hip_stream) {
+    if (!out || !lse || !qkv) return fail(GPT2_EINVAL, "null pointer");
+    if (!aligned16(out) || !aligned16(qkv) || !aligned16(lse))
+        return fail(GPT2_EINVAL, "misaligned pointer");
+    if (dtype != GPT2_DTYPE_FP32 && dtype != GPT2_DTYPE_BF16)
+        return fail(GPT2_EINVAL, "dtype must be 0 or 1");
+    if (B <= 0 || T <= 0 || C <= 0 || NH <= 0)
+        return fail(GPT2_ESHAPE, "B, T, C, NH must be positive");
+    if (C % 8 != 0 || C > 2048 || C % NH != 0 || (C / NH) % 8 != 0 || C / NH > 128)
+        return fail(GPT2_ESHAPE, "need C % 8 == 0, C <= 2048, head size C/NH a multiple of 8, at most 128");
+    if ((int64_t)B * T > 524288 || (int64_t)B * NH > 65535)
+        return fail(GPT2_ESHAPE, "need B*T <= 524288 and B*NH <= 65535");
+    const hipStream_t st = (hipStream_t)hip_stream;
+    if (dtype == GPT2_DTYPE_BF16)
+        attention_fwd<bf16>((bf16*)out, lse, (const bf16*)qkv, B, T, C, NH, st);
+    else
+        attention_fwd<float>((float*)out, lse, (const float*)qkv, B, T, C, NH, st);
+    return hip_status("gpt2_attention_forward");
+}
+
 }  // extern "C"

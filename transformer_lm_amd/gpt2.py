@@ -31,7 +31,7 @@ EXPORTS = ("gpt2_num_params", "gpt2_num_param_tensors", "gpt2_param_table",
            "gpt2_region", "gpt2_act", "gpt2_free",
            "gpt2_last_error", "gpt2_timing_arm", "gpt2_timing_classes", "gpt2_timing_read",
            "gpt2_fp8_scale_workspace_bytes", "gpt2_fp8_scale", "gpt2_fp8_quantize",
-           "gpt2_fp8_matmul")
+           "gpt2_fp8_matmul", "gpt2_attention_forward")
 
 
 class Config(ct.Structure):
@@ -80,6 +80,8 @@ _SIG = {
     "gpt2_fp8_quantize": (ct.c_int, [_P, _P, _P, ct.c_int64, _P]),
     "gpt2_fp8_matmul": (ct.c_int, [_P, _P, _P, _P, _P, ct.c_int32, ct.c_int32, ct.c_int32,
                                    _P]),
+    "gpt2_attention_forward": (ct.c_int, [_P, _P, _P, ct.c_int32, ct.c_int32, ct.c_int32,
+                                          ct.c_int32, ct.c_int32, _P]),
 }
 for _name, (_res, _args) in _SIG.items():
     _f = getattr(_lib, _name)
@@ -323,3 +325,26 @@ def fp8_matmul(out, qx, qw, scales, bias=None, stream=None):
     _check(_lib.gpt2_fp8_matmul(out.data_ptr(), qx.data_ptr(), qw.data_ptr(), scales.data_ptr(),
                                 None if bias is None else bias.data_ptr(), M, N, K,
                                 _stream_of(out, stream)))
+
+
+def attention_forward(out, lse, qkv, NH, stream=None):
+    """Causal self-attention: qkv (B, T, 3C) -> out (B, T, C), lse (B, NH, T)
+    fp32 (natural log); bf16 or fp32 device tensors, out of qkv's dtype."""
+    import torch
+    B, T, C3 = qkv.shape
+    C = C3 // 3
+    if C3 != 3 * C or tuple(out.shape) != (B, T, C) or tuple(lse.shape) != (B, NH, T):
+        raise ValueError("shape mismatch")
+    if out.dtype != qkv.dtype or lse.dtype != torch.float32:
+        raise ValueError("out must have qkv's dtype and lse must be float32")
+    if qkv.dtype == torch.bfloat16:
+        dtype = DTYPE_BF16
+    elif qkv.dtype == torch.float32:
+        dtype = DTYPE_FP32
+    else:
+        raise ValueError("qkv must be bfloat16 or float32")
+    for t in (out, lse, qkv):
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    _check(_lib.gpt2_attention_forward(out.data_ptr(), lse.data_ptr(), qkv.data_ptr(), B, T, C, NH,
+                                       dtype, _stream_of(qkv, stream)))

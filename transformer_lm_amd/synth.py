@@ -141,3 +141,24 @@ def fp8_operands(M, N, K, seed=20240):
     _fill_normal(w, seed + 1, 0, 0.02)
     _fill_normal(b, seed + 2, 0, 0.02)
     return x.reshape(M, K), w.reshape(N, K), b
+
+
+def attention_qkv(B, T, NH, seed=31337):
+    """Fused (B, T, 3C) float32 attention inputs, head size 64, whose scaled
+    scores q_t . k_t' / 8 follow a per-head key profile f(t') plus small
+    noise: head 0 rises by 0.1 per key, head 1 steps up by 6.25 at key 128,
+    head 2 rises by 0.055 per key (q_t = 4e + 0.25 n, k_t' = 2 f(t') e +
+    0.25 n' with e the unit vector of equal entries); other heads draw plain
+    N(0, 1) queries and keys. Values ~ N(0, 1)."""
+    hs = 64
+    n = np.empty(B * T * 3 * NH * hs, np.float32)
+    _fill_normal(n, seed, 0, 1.0)
+    n = n.reshape(B, T, 3, NH, hs)
+    qkv = n.copy()
+    e = np.full(hs, 1.0 / 8.0, np.float32)
+    t = np.arange(T, dtype=np.float32)
+    profiles = (0.1 * t, np.where(t >= 128, 6.25, 0.0).astype(np.float32), 0.055 * t)
+    for h, f in enumerate(profiles[:NH]):
+        qkv[:, :, 0, h] = 4.0 * e + 0.25 * n[:, :, 0, h]
+        qkv[:, :, 1, h] = 2.0 * f[None, :, None] * e + 0.25 * n[:, :, 1, h]
+    return qkv.reshape(B, T, 3 * NH * hs)
