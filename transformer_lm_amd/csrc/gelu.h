@@ -24,13 +24,13 @@ __device__ __forceinline__ float gelu_sigmoid_2a(float x) {
 
 __device__ __forceinline__ float gelu_fast(float x) { return x * gelu_sigmoid_2a(x); }
 
-// g' = s + w (1 - s) with w = 2 x s da/dx and 2 da/dx = 2 sqrt(2/pi) + 6 *
-// 0.044715 sqrt(2/pi) x^2: x^2 shared with the sigmoid's argument, nine VALU
-// operations and the two hardware transcendentals.
+// g' = s + (2 x da/dx) s (1 - s) with 2 da/dx = 2 sqrt(2/pi) + 6 * 0.044715
+// sqrt(2/pi) x^2: x^2 shared with the sigmoid's argument, s (1 - s) one fma,
+// eight VALU operations and the two hardware transcendentals.
 __device__ __forceinline__ float gelu_grad_fast(float x) {
     constexpr float c1 = GELU_M2LOG2E * GELU_K, c2 = c1 * GELU_C;
     const float x2 = x * x;
     const float s = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(x * fmaf(c2, x2, c1)));
-    const float w = x * s * fmaf(6.f * GELU_C * GELU_K, x2, 2.f * GELU_K);
-    return fmaf(-w, s, w) + s;
+    const float xd = x * fmaf(6.f * GELU_C * GELU_K, x2, 2.f * GELU_K);
+    return fmaf(xd, fmaf(-s, s, s), s);
 }
