@@ -1,11 +1,14 @@
 """Training throughput of the GPT-2 124M step (bf16, fp32 master weights and
 AdamW moments, B=16, T=1024) on one MI355X, through the C ABI.
 
-One step = forward (with the mean loss) + backward + AdamW update, on seeded
-synthetic Zipf(1.1) tokens, inputs resident in HBM before timing starts.
-Prints one JSON line: tokens/s, MFU against the bf16 dense peak, the dominant
-kernel class against its roofline (HIP-event durations measured in the timed
-steps), and the CPU oracle timed on a bounded sample of the same workload.
+One step = the upload of the step's tokens from pinned host memory (2 x 64 KB)
++ forward with the mean loss read back + backward + AdamW update, on seeded
+synthetic Zipf(1.1) tokens; parameters and activations are resident in HBM.
+Prints one JSON line: tokens/s over the K timed steps (and the median and
+minimum per-step time), MFU against the bf16 dense peak, every kernel class
+against its roofline (HIP events in a profiled warmup step), the dominant
+class measured again inside the timed steps, and the CPU oracle timed on a
+bounded sample of the same workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-fp8]
 
@@ -17,6 +20,7 @@ import json
 import os
 import sys
 import time
+from dataclasses import replace
 
 import numpy as np
 
@@ -56,28 +60,62 @@ def recorded_traffic(cls):
             "bytes": round(rows[cls][0] + rows[cls][1])}
 
 
-def cpu_baseline(w, T_sample=1024):
-    """The oracle (fp64, plain loops, OpenMP over independent outputs) on one
-    sequence of T_sample tokens of the same model: one full training step."""
-    import oracle
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_step_seconds(w, threads, precision="f32n"):
+    """Seconds of one training step (forward with loss, backward, AdamW) of the
+    oracle on workload w's first batch."""
     from oracle.wrapper import Oracle
     from transformer_lm_amd import synth
-    oracle.build(force=False)
-    ws = w.with_batch(B=1, T=T_sample, steps=1)
-    p = synth.init_params(ws)
-    x, y = synth.split_batch(synth.tokens(ws)[0])
-    threads = len(os.sched_getaffinity(0))
-    o = Oracle(ws, p, threads=threads)
+    p = synth.init_params(w)
+    x, y = synth.split_batch(synth.tokens(w, steps=1)[0])
+    o = Oracle(w, p, precision=precision, threads=threads)
     t0 = time.perf_counter()
     o.forward(x, y)
     o.backward()
     o.update(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, 1)
     dt = time.perf_counter() - t0
-    cores = o.lib.oracle_get_threads()
+    used = o.lib.oracle_get_threads()
     o.close()
-    return {"value": ws.BT / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"one training step (fwd+bwd+AdamW) of the same 124M model on 1 sequence "
-                      f"of {T_sample} tokens, fp64 oracle, {dt:.1f} s"}
+    return dt, used
+
+
+def cpu_baseline(w, T_sample=1024, single_thread=True):
+    """The oracle as it stands (plain loops; OpenMP over independent outputs),
+    built in single precision with -O2 -march=native -fopenmp
+    -ffp-contract=off and no fast math, timed on this host:
+      - value: one training step of the same model on one sequence of T_sample
+        tokens, on every thread the process may use (OMP_NUM_THREADS if set);
+      - single_thread: one step of the tiny model (B=4, T=16) and of the 124M
+        model at B=4, T=64 on one thread."""
+    import oracle
+    from transformer_lm_amd.workloads import WORKLOADS
+    oracle.build(force=True, precisions=("f32n",))
+    threads = int(os.environ.get("OMP_NUM_THREADS", 0)) or len(os.sched_getaffinity(0))
+    ws = w.with_batch(B=1, T=T_sample, steps=1)
+    dt, used = _oracle_step_seconds(replace(ws, dtype="fp32"), threads)
+    out = {"value": round(ws.BT / dt, 2), "unit": "tokens/s", "cores": used, "kind": "oracle",
+           "sample": f"one training step (forward with loss, backward, AdamW) of the same "
+                     f"124M model on 1 sequence of {T_sample} tokens: fp32 oracle built -O2 "
+                     f"-march=native -fopenmp -ffp-contract=off, {used} threads, {dt:.1f} s",
+           "cpu_model": _cpu_model(), "nproc": os.cpu_count()}
+    if single_thread:
+        st = {}
+        for name in ("tiny", "gpt2_124m_fp32"):
+            wn = WORKLOADS[name]
+            d1, _ = _oracle_step_seconds(wn, 1)
+            st[name] = {"B": wn.B, "T": wn.T, "tokens_per_s": round(wn.BT / d1, 2),
+                        "step_s": round(d1, 3)}
+        out["single_thread"] = st
+    return out
 
 
 def fp8_leg(torch, gpt2, synth, M=16384, C=768, V=50304, reps=10):
@@ -143,6 +181,20 @@ def fp8_leg(torch, gpt2, synth, M=16384, C=768, V=50304, reps=10):
     }
 
 
+def class_table(prof):
+    """Per kernel class, from one event-timed step: launches, ms per step, the
+    algorithmic work rate and its fraction of the class's roofline."""
+    out = {}
+    for k, (n, ms, wk, isb) in sorted(prof.items(), key=lambda kv: -kv[1][1]):
+        rate = wk / (ms * 1e-3)
+        peak = PEAK_HBM_BYTES if isb else PEAK_BF16_FLOPS
+        out[k] = {"launches": n, "ms_per_step": round(ms, 4),
+                  "achieved": round(rate / (1e9 if isb else 1e12), 1),
+                  "unit": "GB/s" if isb else "TFLOP/s", "bound": "hbm" if isb else "mfma",
+                  "frac": round(rate / peak, 4)}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -171,22 +223,32 @@ def main():
         f"{args.warmup} warmup + {args.steps} timed steps")
     params = synth.init_params(w)
     toks = synth.tokens(w, steps=max(total, 1))
-    dev_in = [torch.from_numpy(np.ascontiguousarray(toks[s][:, :-1])).cuda() for s in range(total)]
-    dev_tg = [torch.from_numpy(np.ascontiguousarray(toks[s][:, 1:])).cuda() for s in range(total)]
+    # every step's tokens wait in pinned host memory; each step uploads its
+    # inputs and targets (2 x B*T int32) before the forward, as a data loader
+    # feeding the step would
+    host_in = [torch.from_numpy(np.ascontiguousarray(toks[s][:, :-1])).pin_memory()
+               for s in range(total)]
+    host_tg = [torch.from_numpy(np.ascontiguousarray(toks[s][:, 1:])).pin_memory()
+               for s in range(total)]
+    dev_in = torch.empty((w.B, w.T), dtype=torch.int32, device="cuda")
+    dev_tg = torch.empty((w.B, w.T), dtype=torch.int32, device="cuda")
     model = gpt2.GPT2(gpt2.config(w), params)
+    del params
     stream = model.stream
-    loss_dev = torch.zeros(total, dtype=torch.float32, device="cuda")
-    loss_view = model.act("loss")
+    losses = []
 
     def step(s):
-        model.forward(dev_in[s], dev_tg[s], want_loss=False)
-        loss_dev[s].copy_(loss_view[0])
+        with torch.cuda.stream(stream):
+            dev_in.copy_(host_in[s], non_blocking=True)
+            dev_tg.copy_(host_tg[s], non_blocking=True)
+        losses.append(model.forward(dev_in, dev_tg))   # reads the loss (synchronises)
         model.backward()
         model.update(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, s + 1)
 
     # warmup: one step (the second, if there are two) records every kernel
-    # class to find the dominant one
+    # class with HIP events, for the per-class table and the dominant class
     pidx = 1 if args.warmup >= 2 else 0
+    prof = {}
     for s in range(args.warmup):
         if s == pidx:
             model.timing_arm("", 8192)
@@ -195,34 +257,35 @@ def main():
             prof = model.timing_read()
             model.timing_arm(None)
     torch.cuda.synchronize()
-    if args.warmup == 0:
-        prof = {}
-    dominant = max(prof, key=lambda k: prof[k][1]) if prof else "matmul"
-    for k, (n, ms, wk, isb) in sorted(prof.items(), key=lambda kv: -kv[1][1]):
-        rate = wk / (ms * 1e-3) / (1e9 if isb else 1e12)
-        log(f"[bench] warmup profile {k:15s} {n:4d} launches {ms:9.3f} ms  "
-            f"{rate:8.1f} {'GB/s' if isb else 'TFLOP/s'}")
+    classes = class_table(prof)
+    dominant = next(iter(classes)) if classes else "matmul"
+    for k, c in classes.items():
+        log(f"[bench] warmup profile {k:15s} {c['launches']:4d} launches "
+            f"{c['ms_per_step']:9.3f} ms  {c['achieved']:8.1f} {c['unit']} "
+            f"({100 * c['frac']:.1f}% of peak)")
 
-    # timed region: events bracket only the dominant class's launches
+    # timed region: K steps between synchronisations; an event at every step
+    # boundary on the handle's stream gives the per-step times, and events
+    # bracket the dominant class's launches
     model.timing_arm(dominant, 4096)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for s in range(args.warmup, total):
+    for i, s in enumerate(range(args.warmup, total)):
+        evs[i].record(stream)
         step(s)
-    ev1.record(stream)
+    evs[-1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    gpu_ms = ev0.elapsed_time(ev1)
+    step_ms = [evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]
     dom = model.timing_read().get(dominant)
-    losses = loss_dev.cpu().tolist()
 
     ms_per_step = wall * 1e3 / max(args.steps, 1)
     tok_s = w.BT * args.steps / wall
     mfu = tok_s * w.flops_per_token() / PEAK_BF16_FLOPS
-    log(f"[bench] {ms_per_step:.2f} ms/step (events {gpu_ms / max(args.steps, 1):.2f}), "
+    med = float(np.median(step_ms)) if step_ms else None
+    mn = float(np.min(step_ms)) if step_ms else None
+    log(f"[bench] {ms_per_step:.2f} ms/step (per-step events: median {med:.2f}, min {mn:.2f}), "
         f"{tok_s:,.0f} tokens/s, MFU {100 * mfu:.2f}%")
     log("[bench] loss per step: " + " ".join(f"{v:.4f}" for v in losses))
 
@@ -262,7 +325,10 @@ def main():
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample ...")
         cpu = cpu_baseline(w)
-        log(f"[bench] cpu baseline: {cpu['value']:.1f} tokens/s on {cpu['cores']} threads")
+        log(f"[bench] cpu baseline: {cpu['value']:.1f} tokens/s on {cpu['cores']} threads "
+            f"({cpu['cpu_model']}); single thread: " +
+            ", ".join(f"{k} {v['tokens_per_s']:.1f} tokens/s"
+                      for k, v in cpu.get("single_thread", {}).items()))
 
     out = {
         "metric": "train tokens/s, GPT-2 124M bf16 B=16 T=1024, 1 MI355X; MFU %",
@@ -272,19 +338,23 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 3),
+        "ms_per_step_median": round(med, 3) if med is not None else None,
+        "ms_per_step_min": round(mn, 3) if mn is not None else None,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic: seeded Zipf(1.1) tokens over 50257 ids, seeded N(0,0.02) init",
+        "data": "synthetic: seeded Zipf(1.1) tokens over 50257 ids, seeded N(0,0.02) init; "
+                "each step uploads its tokens from pinned host memory and reads its loss",
         "config": {"workload": f"GPT-2 124M training step (forward, backward, AdamW), bf16 "
                                f"activations with fp32 master weights and moments, "
                                f"B={w.B} T={w.T}",
                    "global_batch": w.B, "seq_len": w.T, "parallelism": "single GPU"},
         "mfu": round(mfu, 4),
         "flops_per_token": w.flops_per_token(),
-        "loss_first_last": [round(losses[0], 4), round(losses[-1], 4)] if losses else None,
+        "losses": [round(v, 4) for v in losses[args.warmup:]],
         "roofline": roofline,
+        "classes": classes,
         "cpu_baseline": cpu,
         "fp8_matmul": fp8,
     }

@@ -40,7 +40,11 @@
  * gpt2_last_error() describes the most recent failure on the calling thread.
  * Host-side validation happens at the call. Token ids are checked on the
  * device: an id outside [0, V) sets a flag (the offending position reads as
- * zero) that the next synchronising call reports as GPT2_ETOKEN.
+ * zero) that the next synchronising call, gpt2_forward with a non-null h_loss,
+ * reports as GPT2_ETOKEN. The flag holds the number of the forward call that
+ * saw the id, so a forward issued without h_loss is named in the message when
+ * a later checked forward reports it; after GPT2_ETOKEN, gpt2_backward is
+ * refused until the next forward.
  */
 #ifndef GPT2_H
 #define GPT2_H
@@ -272,6 +276,24 @@ int gpt2_fp8_matmul(void* out, const uint8_t* qx, const uint8_t* qw, const float
  */
 int gpt2_attention_forward(void* out, float* lse, const void* qkv, int32_t B, int32_t T,
                            int32_t C, int32_t NH, int32_t dtype, void* hip_stream);
+
+/* Gradient of the same attention (page "llm.c: Large Language Model Training
+ * in Pure C/CUDA Without Dependencies", section "Exact Analytical Backward
+ * Pass", softmax backward; the kernels gpt2_backward runs), on caller-owned
+ * buffers and without a handle. With P the causal probabilities rebuilt from
+ * lse, dP = dout v^T, D_t = sum_d dout[t,d] out[t,d] and dS = P (dP - D):
+ *   dq = dS k / sqrt(hs), dk = dS^T q / sqrt(hs), dv = P^T dout.
+ *   dqkv (B, T, 3C) dtype-typed, written (every element: the q, k and v
+ *        channel gradients in qkv's layout);
+ *   work fp32 workspace of B*NH*T floats (the rows' D), caller-owned;
+ *   dout (B, T, C) the gradient of out, dtype-typed;
+ *   qkv, out, lse as gpt2_attention_forward takes and produced them.
+ * Asynchronous on hip_stream. Pointers 16-byte aligned. Returns GPT2_OK,
+ * GPT2_EINVAL, GPT2_ESHAPE (the limits of gpt2_attention_forward) or
+ * GPT2_EHIP (launch failed). */
+int gpt2_attention_backward(void* dqkv, float* work, const void* dout, const void* qkv,
+                            const void* out, const float* lse, int32_t B, int32_t T, int32_t C,
+                            int32_t NH, int32_t dtype, void* hip_stream);
 
 /* Message for the most recent failure on this thread ("" if none). */
 const char* gpt2_last_error(void);

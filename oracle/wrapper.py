@@ -10,20 +10,25 @@ SRC = os.path.join(HERE, "gpt2_oracle.c")
 _LIBS = {}
 
 
+# builds: the double-precision parity reference, a portable float build, and
+# the float build for timing on the host it runs on (-march=native, no fast
+# math, no contraction: the same arithmetic, vectorised where the compiler may)
+BUILDS = {"f64": ("double", []), "f32": ("float", []), "f32n": ("float", ["-march=native"])}
+
+
 def lib_path(precision="f64"):
     return os.path.join(HERE, f"liboracle_{precision}.so")
 
 
-def build(force=True, native=False):
-    """Compile both oracle builds. `native` adds -march=native (host timing)."""
-    for prec, real in (("f64", "double"), ("f32", "float")):
+def build(force=True, precisions=("f64", "f32")):
+    """Compile the oracle builds named in `precisions` (keys of BUILDS)."""
+    for prec in precisions:
+        real, extra = BUILDS[prec]
         out = lib_path(prec)
         if not force and os.path.exists(out) and os.path.getmtime(out) >= os.path.getmtime(SRC):
             continue
         cmd = ["gcc", "-std=c99", "-O2", "-fopenmp", "-ffp-contract=off", "-fPIC",
-               "-shared", f"-DREAL={real}", "-Wall", "-Wno-unknown-pragmas"]
-        if native:
-            cmd.append("-march=native")
+               "-shared", f"-DREAL={real}", "-Wall", "-Wno-unknown-pragmas"] + extra
         tmp = out + ".tmp"
         subprocess.run(cmd + [SRC, "-o", tmp, "-lm"], check=True)
         os.replace(tmp, out)
@@ -38,7 +43,7 @@ def load(precision="f64"):
         return _LIBS[precision]
     path = lib_path(precision)
     if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(SRC):
-        build(force=False)
+        build(force=False, precisions=(precision,))
     lib = ct.CDLL(path)
     real = ct.c_double if lib.oracle_real_bytes() == 8 else ct.c_float
     lib._real = real
@@ -296,3 +301,19 @@ def attention_forward(qkv, NH):
     lib.oracle_attention_forward(ptr(out, ct.c_double), ptr(att, ct.c_double),
                                  ptr(qkv, ct.c_double), B, T, C, NH)
     return out, att
+
+
+def attention_backward(qkv, dout, NH):
+    """The oracle's attention gradient: dqkv (B, T, 3C) float64 for the
+    output gradient dout (B, T, C) of the causal attention of qkv."""
+    lib = load()
+    qkv = np.ascontiguousarray(qkv, np.float64)
+    dout = np.ascontiguousarray(dout, np.float64)
+    B, T, C3 = qkv.shape
+    C = C3 // 3
+    assert dout.shape == (B, T, C)
+    _, att = attention_forward(qkv, NH)
+    dqkv = np.zeros((B, T, C3), np.float64)
+    lib.oracle_attention_backward(ptr(dqkv, ct.c_double), ptr(dout, ct.c_double),
+                                  ptr(qkv, ct.c_double), ptr(att, ct.c_double), B, T, C, NH)
+    return dqkv

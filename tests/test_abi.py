@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(g):
     names = declared_functions()
-    assert len(names) == 26
+    assert len(names) == 27
     lib = ct.CDLL(g.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -134,4 +134,19 @@ def test_attention_entry_point_validates_before_launching(g):
     assert att(a, a, a, 1, 8, 512, 2, bf16, None) == g.GPT2_ESHAPE         # head size 256
     assert att(a, a, a, 1, 8, 128, 3, bf16, None) == g.GPT2_ESHAPE         # C % NH
     assert att(a, a, a, 1024, 1024, 128, 2, bf16, None) == g.GPT2_ESHAPE   # B*T
+    assert g.last_error()
+
+
+def test_attention_backward_entry_point_validates_before_launching(g):
+    att = g._lib.gpt2_attention_backward
+    a = 1 << 20                                      # 16-byte aligned, never dereferenced
+    bf16 = g.DTYPE_BF16
+    assert att(None, a, a, a, a, a, 1, 8, 128, 2, bf16, None) == g.GPT2_EINVAL
+    assert att(a, None, a, a, a, a, 1, 8, 128, 2, bf16, None) == g.GPT2_EINVAL   # no workspace
+    assert att(a, a, a, a, a, None, 1, 8, 128, 2, bf16, None) == g.GPT2_EINVAL
+    assert att(a, a, a + 2, a, a, a, 1, 8, 128, 2, bf16, None) == g.GPT2_EINVAL  # dout misaligned
+    assert att(a, a, a, a, a, a, 1, 8, 128, 2, 5, None) == g.GPT2_EINVAL         # dtype
+    assert att(a, a, a, a, a, a, 0, 8, 128, 2, bf16, None) == g.GPT2_ESHAPE
+    assert att(a, a, a, a, a, a, 1, 8, 120, 2, bf16, None) == g.GPT2_ESHAPE      # head size 60
+    assert att(a, a, a, a, a, a, 1024, 1024, 128, 2, bf16, None) == g.GPT2_ESHAPE  # B*T
     assert g.last_error()

@@ -232,3 +232,17 @@ def test_out_of_range_token_is_rejected(oracle_lib):
     x[0, 0] = w.V                     # a padded id is not a token
     with pytest.raises(ValueError):
         Oracle(w, p).forward(x, y)
+
+
+def test_nan_poisoned_parameter_gives_a_non_finite_loss(oracle_lib):
+    """A NaN in a parameter that the step reads (a LayerNorm gain of the first
+    block) propagates: the loss and the gradients are NaN; no error code,
+    since nothing about the call is invalid."""
+    w, p, x, y = _setup("tiny")
+    off, _ = param_offsets(w)["ln1w"]
+    p = p.copy()
+    p[off + 3] = np.nan
+    o = Oracle(w, p)
+    assert np.isnan(o.forward(x, y))
+    o.backward()
+    assert np.isnan(o.grads()).any()

@@ -16,7 +16,7 @@ __global__ __launch_bounds__(CL_THREADS) void classifier_kernel(T* logits,
                                                                 float* __restrict__ losses,
                                                                 const int32_t* __restrict__ targets,
                                                                 int V, int Vp, float dloss,
-                                                                int* err) {
+                                                                int* err, int tag) {
     __shared__ float red[16];
     const int64_t row = blockIdx.x;
     T* z = logits + row * Vp;
@@ -44,7 +44,7 @@ __global__ __launch_bounds__(CL_THREADS) void classifier_kernel(T* logits,
             losses[row] = lse - to_f32(z[tgt]);
         } else {
             losses[row] = 0.f;
-            atomicOr(err, 1);
+            atomicMax(err, tag);
         }
     }
     __syncthreads();  // the target logit is read before any thread overwrites it
@@ -110,7 +110,7 @@ __device__ __forceinline__ void store8_nt(T* p, const float (&v)[8]) {
 template <typename T, int NCHK>
 __global__ __launch_bounds__(CL_THREADS) void classifier_reg_kernel(
     T* logits, float* __restrict__ losses, const int32_t* __restrict__ targets, int V, int Vp,
-    float dloss, int* err) {
+    float dloss, int* err, int tag) {
     __shared__ float red[16];
     const int64_t row = blockIdx.x;
     T* z = logits + row * Vp;
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(CL_THREADS) void classifier_reg_kernel(
         if ((int)threadIdx.x == own) losses[row] = lse - zt;
     } else if (threadIdx.x == 0) {
         losses[row] = 0.f;
-        atomicOr(err, 1);
+        atomicMax(err, tag);
     }
     const float l2 = lse * CL_LOG2E;
 #pragma unroll
@@ -195,16 +195,16 @@ __global__ __launch_bounds__(CL_THREADS) void classifier_reg_kernel(
 
 template <typename T>
 void classifier_fwd(T* logits, float* losses, const int32_t* targets, int N, int V, int Vp,
-                    float dloss, int* err, hipStream_t st) {
+                    float dloss, int* err, int tag, hipStream_t st) {
     const int nchk = ceil_div(Vp, 8 * CL_THREADS);
     if (nchk <= 1)
-        classifier_reg_kernel<T, 1><<<N, CL_THREADS, 0, st>>>(logits, losses, targets, V, Vp, dloss, err);
+        classifier_reg_kernel<T, 1><<<N, CL_THREADS, 0, st>>>(logits, losses, targets, V, Vp, dloss, err, tag);
     else if (nchk <= 4)
-        classifier_reg_kernel<T, 4><<<N, CL_THREADS, 0, st>>>(logits, losses, targets, V, Vp, dloss, err);
+        classifier_reg_kernel<T, 4><<<N, CL_THREADS, 0, st>>>(logits, losses, targets, V, Vp, dloss, err, tag);
     else if (nchk <= 7)
-        classifier_reg_kernel<T, 7><<<N, CL_THREADS, 0, st>>>(logits, losses, targets, V, Vp, dloss, err);
+        classifier_reg_kernel<T, 7><<<N, CL_THREADS, 0, st>>>(logits, losses, targets, V, Vp, dloss, err, tag);
     else
-        classifier_kernel<T><<<N, CL_THREADS, 0, st>>>(logits, losses, targets, V, Vp, dloss, err);
+        classifier_kernel<T><<<N, CL_THREADS, 0, st>>>(logits, losses, targets, V, Vp, dloss, err, tag);
 }
 
 __global__ __launch_bounds__(1024) void loss_mean_kernel(float* out, const float* __restrict__ l,
@@ -221,6 +221,6 @@ void loss_mean(float* out, const float* losses, int n, hipStream_t st) {
 }
 
 template void classifier_fwd<float>(float*, float*, const int32_t*, int, int, int, float, int*,
-                                    hipStream_t);
+                                    int, hipStream_t);
 template void classifier_fwd<bf16>(bf16*, float*, const int32_t*, int, int, int, float, int*,
-                                   hipStream_t);
+                                   int, hipStream_t);

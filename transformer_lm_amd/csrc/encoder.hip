@@ -7,7 +7,8 @@ __global__ __launch_bounds__(256) void encoder_fwd_kernel(T* __restrict__ out,
                                                           const int32_t* __restrict__ tok,
                                                           const T* __restrict__ wte,
                                                           const T* __restrict__ wpe, int BT,
-                                                          int Tn, int C, int V, int* err) {
+                                                          int Tn, int C, int V, int* err,
+                                                          int tag) {
     const int c8n = C / 8;
     int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
     if (idx >= (int64_t)BT * c8n) return;
@@ -16,7 +17,7 @@ __global__ __launch_bounds__(256) void encoder_fwd_kernel(T* __restrict__ out,
     int id = tok[bt];
     float v[8];
     if (id < 0 || id >= V) {
-        if (c == 0) atomicOr(err, 1);
+        if (c == 0) atomicMax(err, tag);
 #pragma unroll
         for (int k = 0; k < 8; k++) v[k] = 0.f;
     } else {
@@ -31,10 +32,10 @@ __global__ __launch_bounds__(256) void encoder_fwd_kernel(T* __restrict__ out,
 
 template <typename T>
 void encoder_fwd(T* out, const int32_t* tok, const T* wte, const T* wpe, int B, int Tn, int C,
-                 int V, int* err, hipStream_t st) {
+                 int V, int* err, int tag, hipStream_t st) {
     int64_t n = (int64_t)B * Tn * (C / 8);
     encoder_fwd_kernel<T><<<ceil_div(n, 256), 256, 0, st>>>(out, tok, wte, wpe, B * Tn, Tn, C,
-                                                            V, err);
+                                                            V, err, tag);
 }
 
 // dwpe[t, c] = sum_b dout[b, t, c] in increasing b; rows t >= Tn are zeroed.
@@ -350,9 +351,9 @@ void encoder_bwd(float* dwte, float* dwpe, const T* dout, const int32_t* tok, in
 }
 
 template void encoder_fwd<float>(float*, const int32_t*, const float*, const float*, int, int,
-                                 int, int, int*, hipStream_t);
+                                 int, int, int*, int, hipStream_t);
 template void encoder_fwd<bf16>(bf16*, const int32_t*, const bf16*, const bf16*, int, int, int,
-                                int, int*, hipStream_t);
+                                int, int*, int, hipStream_t);
 template void encoder_bwd<float>(float*, float*, const float*, const int32_t*, int, int, int, int,
                                  int, void*, hipStream_t);
 template void encoder_bwd<bf16>(float*, float*, const bf16*, const int32_t*, int, int, int, int,

@@ -28,6 +28,8 @@ int fail(int code, const char* msg) {
     return code;
 }
 
+int fail(int code, const std::string& msg) { return fail(code, msg.c_str()); }
+
 enum {
     P_WTE, P_WPE, P_LN1W, P_LN1B, P_QKVW, P_QKVB, P_ATTPROJW, P_ATTPROJB,
     P_LN2W, P_LN2B, P_FCW, P_FCB, P_FCPROJW, P_FCPROJB, P_LNFW, P_LNFB, NUM_P
@@ -195,6 +197,7 @@ struct gpt2 {
     float* gp[NUM_P];  // parameter gradients
     void* a[NUM_A];
     bool fwd_targets;
+    int fwd_count;  // forwards issued so far; tags a token error with its call
     const int32_t* last_inputs;
     // timing
     bool tarm[NUM_K];
@@ -273,7 +276,7 @@ void forward_impl(gpt2* h, const int32_t* in, const int32_t* tg) {
 
     {
         KScope k(h, K_ENCODER_FWD, 3.0 * nC * es + 4.0 * BT);
-        encoder_fwd<T>(encoded, in, P[P_WTE], P[P_WPE], B, Tn, C, V, err, st);
+        encoder_fwd<T>(encoded, in, P[P_WTE], P[P_WPE], B, Tn, C, V, err, h->fwd_count, st);
     }
     for (int l = 0; l < L; l++) {
         const T* res = l == 0 ? encoded : res3 + (l - 1) * nC;
@@ -336,13 +339,13 @@ void forward_impl(gpt2* h, const int32_t* in, const int32_t* tg) {
     }
     T* logits = (T*)h->a[A_LOGITS];
     {
-        KScope k(h, K_MATMUL_FWD, mm_flops(BT, Vp, C));
+        KScope k(h, K_MATMUL_FWD, mm_flops(BT, V, C));
         matmul_fwd<T>(logits, lnf, P[P_WTE], nullptr, nullptr, BT, C, Vp, st);
     }
     if (tg) {
         KScope k(h, K_CLASSIFIER, 2.0 * BT * (double)Vp * es + 8.0 * BT);
         float* losses = (float*)h->a[A_LOSSES];
-        classifier_fwd<T>(logits, losses, tg, BT, V, Vp, 1.f / (float)BT, err, st);
+        classifier_fwd<T>(logits, losses, tg, BT, V, Vp, 1.f / (float)BT, err, h->fwd_count, st);
         loss_mean((float*)h->a[A_LOSS], losses, BT, st);
     }
 }
@@ -350,7 +353,7 @@ void forward_impl(gpt2* h, const int32_t* in, const int32_t* tg) {
 template <typename T>
 void backward_impl(gpt2* h) {
     const gpt2_config& c = h->cfg;
-    const int B = c.B, Tn = c.T, C = c.C, L = c.L, NH = c.NH, Vp = c.Vp;
+    const int B = c.B, Tn = c.T, C = c.C, L = c.L, NH = c.NH, V = c.V, Vp = c.Vp;
     const int BT = B * Tn;
     const int64_t nC = (int64_t)BT * C;
     const double es = sizeof(T);
@@ -398,11 +401,11 @@ void backward_impl(gpt2* h) {
     // the same B*T rows, so one launch fills the GPU's rounds of resident
     // tiles better than two.
     {
-        KScope k(h, K_MATMUL_BWD_DX, mm_flops(BT, C, Vp));
+        KScope k(h, K_MATMUL_BWD_DX, mm_flops(BT, C, V));
         matmul_bwd_dx<T>(dC, dlogits, P[P_WTE], BT, Vp, C, st);
     }
     dw_tasks.push_back({dlogits, lnf, G[P_WTE], nullptr, Vp, C});
-    dw_flops += mm_flops(Vp, C, BT);
+    dw_flops += mm_flops(V, C, BT);
     // LayerNorm weight gradients: per-block partial sums now, one batched
     // fixed-order reduction of all 2L+1 LayerNorms after the layer loop
     LnRedBatch ln_red;
@@ -601,14 +604,17 @@ int gpt2_forward(gpt2* h, const int32_t* d_inputs, const int32_t* d_targets, flo
     if (h_loss && !d_targets) return fail(GPT2_EINVAL, "a loss needs targets");
     if ((uintptr_t)d_inputs % 4 || (uintptr_t)d_targets % 4)
         return fail(GPT2_EINVAL, "token arrays must be 4-byte aligned");
+    h->fwd_targets = false;  // until this forward has been issued cleanly
+    h->fwd_count = h->fwd_count == INT32_MAX ? 1 : h->fwd_count + 1;
     if (h->cfg.dtype == GPT2_DTYPE_BF16)
         forward_impl<bf16>(h, d_inputs, d_targets);
     else
         forward_impl<float>(h, d_inputs, d_targets);
-    h->fwd_targets = d_targets != nullptr;
     h->last_inputs = d_inputs;
     int rc = hip_status("gpt2_forward");
-    if (rc != GPT2_OK || !h_loss) return rc;
+    if (rc != GPT2_OK) return rc;
+    h->fwd_targets = d_targets != nullptr;
+    if (!h_loss) return GPT2_OK;
     float loss = 0.f;
     int err = 0;
     if (hipMemcpyAsync(&loss, h->a[A_LOSS], 4, hipMemcpyDeviceToHost, h->st) != hipSuccess ||
@@ -617,8 +623,16 @@ int gpt2_forward(gpt2* h, const int32_t* d_inputs, const int32_t* d_targets, flo
         return fail(GPT2_EHIP, "gpt2_forward: reading the loss failed");
     *h_loss = loss;
     if (err) {
+        // the flag holds the number of the latest forward that saw a bad id;
+        // an unchecked earlier forward is named as such
         fill_zero_i32((int*)h->a[A_ERR], 1, h->st);
-        return fail(GPT2_ETOKEN, "a token id outside [0, V) was seen");
+        h->fwd_targets = false;
+        const int now = h->fwd_count;
+        return fail(GPT2_ETOKEN,
+                    err == now ? std::string("a token id outside [0, V) was seen in this forward")
+                               : "a token id outside [0, V) was seen in forward call " +
+                                     std::to_string(err) + " (not checked then); this is call " +
+                                     std::to_string(now));
     }
     return GPT2_OK;
 }
@@ -888,6 +902,48 @@ int gpt2_attention_forward(void* out, float* lse, const void* qkv, int32_t B, in
     else
         attention_fwd<float>((float*)out, lse, (const float*)qkv, B, T, C, NH, st);
     return hip_status("gpt2_attention_forward");
+}
+
+// Validation shared by the attention backward entry points.
+static int attention_bwd_args(const void* dqkv, const void* dout, const void* qkv, const void* out,
+                              const float* lse, int32_t B, int32_t T, int32_t C, int32_t NH,
+                              int32_t dtype) {
+    if (!dqkv || !dout || !qkv || !out || !lse) return fail(GPT2_EINVAL, "null pointer");
+    if (!aligned16(dqkv) || !aligned16(dout) || !aligned16(qkv) || !aligned16(out) ||
+        !aligned16(lse))
+        return fail(GPT2_EINVAL, "misaligned pointer");
+    if (dtype != GPT2_DTYPE_FP32 && dtype != GPT2_DTYPE_BF16)
+        return fail(GPT2_EINVAL, "dtype must be 0 or 1");
+    if (B <= 0 || T <= 0 || C <= 0 || NH <= 0)
+        return fail(GPT2_ESHAPE, "B, T, C, NH must be positive");
+    if (C % 8 != 0 || C > 2048 || C % NH != 0 || (C / NH) % 8 != 0 || C / NH > 128)
+        return fail(GPT2_ESHAPE, "need C % 8 == 0, C <= 2048, head size C/NH a multiple of 8, at most 128");
+    if ((int64_t)B * T > 524288 || (int64_t)B * NH > 65535)
+        return fail(GPT2_ESHAPE, "need B*T <= 524288 and B*NH <= 65535");
+    return GPT2_OK;
+}
+
+static void attention_bwd_launch(void* dqkv, float* work, const void* dout, const void* qkv,
+                                 const void* out, const float* lse, int B, int T, int C, int NH,
+                                 int dtype, hipStream_t st) {
+    if (dtype == GPT2_DTYPE_BF16)
+        attention_bwd<bf16>((bf16*)dqkv, (const bf16*)dout, (const bf16*)qkv, (const bf16*)out, lse,
+                            work, B, T, C, NH, st);
+    else
+        attention_bwd<float>((float*)dqkv, (const float*)dout, (const float*)qkv,
+                             (const float*)out, lse, work, B, T, C, NH, st);
+}
+
+int gpt2_attention_backward(void* dqkv, float* work, const void* dout, const void* qkv,
+                            const void* out, const float* lse, int32_t B, int32_t T, int32_t C,
+                            int32_t NH, int32_t dtype, void* hip_stream) {
+    const int rc = attention_bwd_args(dqkv, dout, qkv, out, lse, B, T, C, NH, dtype);
+    if (rc != GPT2_OK) return rc;
+    if (!work) return fail(GPT2_EINVAL, "null pointer");
+    if (!aligned16(work)) return fail(GPT2_EINVAL, "misaligned pointer");
+    attention_bwd_launch(dqkv, work, dout, qkv, out, lse, B, T, C, NH, dtype,
+                         (hipStream_t)hip_stream);
+    return hip_status("gpt2_attention_backward");
 }
 
 }  // extern "C"

@@ -6,11 +6,11 @@
 #include "common.h"
 
 // ---- encoder (token + position embedding) ---------------------------------
-// out[b,t,:] = wte[tok[b,t],:] + wpe[t,:]; ids outside [0,V) set *err and
-// produce a zero row.
+// out[b,t,:] = wte[tok[b,t],:] + wpe[t,:]; an id outside [0,V) produces a zero
+// row and raises *err to at least `tag` (the caller's forward number, >= 1).
 template <typename T>
 void encoder_fwd(T* out, const int32_t* tok, const T* wte, const T* wpe, int B, int Tn, int C,
-                 int V, int* err, hipStream_t st);
+                 int V, int* err, int tag, hipStream_t st);
 // dwte[tok[b,t],:] += dout[b,t,:] (deterministic: the positions of one token
 // are summed in increasing order, in a fixed grouping); dwpe[t,:] =
 // sum_b dout[b,t,:], rows >= Tn = 0. ws: encoder_bwd_workspace_bytes(B*Tn,
@@ -140,7 +140,7 @@ void round_to_bf16(bf16* out, const float* in, int64_t n, hipStream_t st);
 // logits overwritten by dz = (softmax - onehot) * dloss (0 on padded columns).
 template <typename T>
 void classifier_fwd(T* logits, float* losses, const int32_t* targets, int N, int V, int Vp,
-                    float dloss, int* err, hipStream_t st);
+                    float dloss, int* err, int tag, hipStream_t st);
 // *out = mean of losses[0..n) (fixed summation order)
 void loss_mean(float* out, const float* losses, int n, hipStream_t st);
 

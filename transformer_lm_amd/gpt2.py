@@ -11,9 +11,8 @@ import os
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-# GPT2_LIB selects another build of the same library (side-by-side timing of
-# two builds in one process tree); the default is the in-tree build.
-LIB_PATH = os.environ.get("GPT2_LIB") or os.path.join(HERE, "libgpt2.so")
+# always the in-tree build, next to this file
+LIB_PATH = os.path.join(HERE, "libgpt2.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run transformer_lm_amd.build.build() "
@@ -31,7 +30,7 @@ EXPORTS = ("gpt2_num_params", "gpt2_num_param_tensors", "gpt2_param_table",
            "gpt2_region", "gpt2_act", "gpt2_free",
            "gpt2_last_error", "gpt2_timing_arm", "gpt2_timing_classes", "gpt2_timing_read",
            "gpt2_fp8_scale_workspace_bytes", "gpt2_fp8_scale", "gpt2_fp8_quantize",
-           "gpt2_fp8_matmul", "gpt2_attention_forward")
+           "gpt2_fp8_matmul", "gpt2_attention_forward", "gpt2_attention_backward")
 
 
 class Config(ct.Structure):
@@ -82,6 +81,8 @@ _SIG = {
                                    _P]),
     "gpt2_attention_forward": (ct.c_int, [_P, _P, _P, ct.c_int32, ct.c_int32, ct.c_int32,
                                           ct.c_int32, ct.c_int32, _P]),
+    "gpt2_attention_backward": (ct.c_int, [_P, _P, _P, _P, _P, _P, ct.c_int32, ct.c_int32,
+                                           ct.c_int32, ct.c_int32, ct.c_int32, _P]),
 }
 for _name, (_res, _args) in _SIG.items():
     _f = getattr(_lib, _name)
@@ -348,3 +349,27 @@ def attention_forward(out, lse, qkv, NH, stream=None):
             raise ValueError("tensors must be contiguous")
     _check(_lib.gpt2_attention_forward(out.data_ptr(), lse.data_ptr(), qkv.data_ptr(), B, T, C, NH,
                                        dtype, _stream_of(qkv, stream)))
+
+
+def attention_backward(dqkv, work, dout, qkv, out, lse, NH, stream=None):
+    """Gradient of causal self-attention: dqkv (B, T, 3C) from dout (B, T, C)
+    and the forward's qkv, out, lse; work: float32 device tensor of B*NH*T."""
+    import torch
+    B, T, C3 = qkv.shape
+    C = C3 // 3
+    if C3 != 3 * C or tuple(out.shape) != (B, T, C) or tuple(dout.shape) != (B, T, C) or \
+            tuple(dqkv.shape) != (B, T, C3) or tuple(lse.shape) != (B, NH, T) or \
+            work.numel() < B * NH * T:
+        raise ValueError("shape mismatch")
+    if len({qkv.dtype, out.dtype, dout.dtype, dqkv.dtype}) != 1 or \
+            lse.dtype != torch.float32 or work.dtype != torch.float32:
+        raise ValueError("qkv, out, dout, dqkv share one dtype; lse and work are float32")
+    dtype = {torch.bfloat16: DTYPE_BF16, torch.float32: DTYPE_FP32}.get(qkv.dtype)
+    if dtype is None:
+        raise ValueError("qkv must be bfloat16 or float32")
+    for t in (dqkv, work, dout, qkv, out, lse):
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    _check(_lib.gpt2_attention_backward(dqkv.data_ptr(), work.data_ptr(), dout.data_ptr(),
+                                        qkv.data_ptr(), out.data_ptr(), lse.data_ptr(), B, T, C,
+                                        NH, dtype, _stream_of(qkv, stream)))

@@ -26,6 +26,8 @@ cumulative table (smallest k with CDF(k) > u). Each optimiser step draws a
 fresh (B, T+1) block; inputs are [:, :T] and targets [:, 1:].
 """
 import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -73,11 +75,22 @@ def normal(seed, start, count):
 
 
 def _fill_normal(out, seed, flat_start, std):
-    """out[i] = std * normal element (flat_start + i), chunked to bound memory."""
+    """out[i] = std * normal element (flat_start + i), in chunks (bounded
+    memory) spread over threads; every element depends only on its index, so
+    the bytes do not depend on the thread count."""
     n = out.size
-    for c0 in range(0, n, _CHUNK):
+
+    def chunk(c0):
         c1 = min(n, c0 + _CHUNK)
         out[c0:c1] = (std * normal(seed, flat_start + c0, c1 - c0)).astype(np.float32)
+
+    starts = range(0, n, _CHUNK)
+    if len(starts) <= 1:
+        for c0 in starts:
+            chunk(c0)
+        return
+    with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1, len(starts))) as ex:
+        list(ex.map(chunk, starts))
 
 
 def init_params(w, seed=None):
@@ -162,3 +175,10 @@ def attention_qkv(B, T, NH, seed=31337):
         qkv[:, :, 0, h] = 4.0 * e + 0.25 * n[:, :, 0, h]
         qkv[:, :, 1, h] = 2.0 * f[None, :, None] * e + 0.25 * n[:, :, 1, h]
     return qkv.reshape(B, T, 3 * NH * hs)
+
+
+def attention_dout(B, T, C, seed=31338):
+    """Output gradient (B, T, C) float32 ~ N(0, 1) for the attention backward."""
+    d = np.empty(B * T * C, np.float32)
+    _fill_normal(d, seed, 0, 1.0)
+    return d.reshape(B, T, C)
