@@ -295,6 +295,23 @@ int gpt2_attention_backward(void* dqkv, float* work, const void* dout, const voi
                             const void* out, const float* lse, int32_t B, int32_t T, int32_t C,
                             int32_t NH, int32_t dtype, void* hip_stream);
 
+/* gpt2_attention_backward for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. It takes no workspace and allocates nothing (no hipMalloc,
+ * hipFree or allocating library call): the rows' D values go to a static
+ * device array of 2^20 floats (4 MiB) that each GPU holds from the first call
+ * on it until the process ends. Needs B*NH*T <= 2^20 (GPT2_ESHAPE otherwise);
+ * other arguments, limits and results as gpt2_attention_backward. Nothing in
+ * the scratch needs to start at zero: every D value a call reads is written
+ * by that call first. Calls on one GPU share its scratch, so calls that
+ * overlap on one GPU (different streams, or host threads) race; calls on one
+ * stream are ordered. The stream must belong to the current device
+ * (GPT2_EINVAL otherwise); the device's scratch address is looked up with it
+ * current on its first call (GPT2_EHIP if that fails). */
+int gpt2_attention_backward_noalloc(void* dqkv, const void* dout, const void* qkv,
+                                    const void* out, const float* lse, int32_t B, int32_t T,
+                                    int32_t C, int32_t NH, int32_t dtype, void* hip_stream);
+
 /* Message for the most recent failure on this thread ("" if none). */
 const char* gpt2_last_error(void);
 

@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(g):
     names = declared_functions()
-    assert len(names) == 27
+    assert len(names) == 28
     lib = ct.CDLL(g.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -150,3 +150,16 @@ def test_attention_backward_entry_point_validates_before_launching(g):
     assert att(a, a, a, a, a, a, 1, 8, 120, 2, bf16, None) == g.GPT2_ESHAPE      # head size 60
     assert att(a, a, a, a, a, a, 1024, 1024, 128, 2, bf16, None) == g.GPT2_ESHAPE  # B*T
     assert g.last_error()
+
+
+def test_noalloc_attention_backward_validates_before_launching(g):
+    att = g._lib.gpt2_attention_backward_noalloc
+    a = 1 << 20                                      # 16-byte aligned, never dereferenced
+    bf16 = g.DTYPE_BF16
+    assert att(None, a, a, a, a, 1, 8, 128, 2, bf16, None) == g.GPT2_EINVAL
+    assert att(a, a, a, a, a + 4, 1, 8, 128, 2, bf16, None) == g.GPT2_EINVAL   # lse misaligned
+    assert att(a, a, a, a, a, 1, 8, 128, 2, 9, None) == g.GPT2_EINVAL          # dtype
+    assert att(a, a, a, a, a, 1, 8, 120, 2, bf16, None) == g.GPT2_ESHAPE       # head size 60
+    # beyond the static scratch: B*NH*T = 65 * 16 * 1024 > 2^20
+    assert att(a, a, a, a, a, 65, 1024, 1024, 16, bf16, None) == g.GPT2_ESHAPE
+    assert "static scratch" in g.last_error()

@@ -13,6 +13,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -932,6 +933,61 @@ static void attention_bwd_launch(void* dqkv, float* work, const void* dout, cons
     else
         attention_bwd<float>((float*)dqkv, (const float*)dout, (const float*)qkv,
                              (const float*)out, lse, work, B, T, C, NH, st);
+}
+
+// Scratch of gpt2_attention_backward_noalloc: the rows' D values, B*NH*T
+// floats at most. A file-scope device array: each GPU the library runs on
+// holds one copy until the process ends. Host code never uses the array's
+// name as an address; it uses the per-device address hipGetSymbolAddress
+// returns, looked up once per device with that device current.
+#define NOALLOC_SCRATCH_FLOATS (1 << 20)
+#define NOALLOC_MAX_DEVICES 64
+static __device__ __align__(256) float scratch[NOALLOC_SCRATCH_FLOATS];
+static std::mutex g_scratch_mu;
+static float* g_scratch_ptr[NOALLOC_MAX_DEVICES];
+
+// Address of the current device's scratch (looked up on its first use).
+static int scratch_of_current_device(float** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(GPT2_EHIP, "hipGetDevice failed");
+    if (dev < 0 || dev >= NOALLOC_MAX_DEVICES)
+        return fail(GPT2_EINVAL, "device index beyond the scratch table");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+            (void)hipGetLastError();
+            return fail(GPT2_EHIP, "hipGetSymbolAddress(scratch) failed");
+        }
+        g_scratch_ptr[dev] = static_cast<float*>(ptr);
+    }
+    *out = g_scratch_ptr[dev];
+    return GPT2_OK;
+}
+
+int gpt2_attention_backward_noalloc(void* dqkv, const void* dout, const void* qkv,
+                                    const void* out, const float* lse, int32_t B, int32_t T,
+                                    int32_t C, int32_t NH, int32_t dtype, void* hip_stream) {
+    int rc = attention_bwd_args(dqkv, dout, qkv, out, lse, B, T, C, NH, dtype);
+    if (rc != GPT2_OK) return rc;
+    const int64_t need = (int64_t)B * NH * T;
+    if (need > NOALLOC_SCRATCH_FLOATS)
+        return fail(GPT2_ESHAPE, "B*NH*T = " + std::to_string(need) +
+                                     " exceeds the static scratch of " +
+                                     std::to_string(NOALLOC_SCRATCH_FLOATS) + " floats");
+    const hipStream_t st = (hipStream_t)hip_stream;
+    if (st) {
+        int cur = -1, sdev = -1;
+        if (hipGetDevice(&cur) != hipSuccess || hipStreamGetDevice(st, &sdev) != hipSuccess)
+            return fail(GPT2_EHIP, "querying the stream's device failed");
+        if (cur != sdev)
+            return fail(GPT2_EINVAL, "the stream belongs to a device other than the current one");
+    }
+    float* work = nullptr;
+    rc = scratch_of_current_device(&work);
+    if (rc != GPT2_OK) return rc;
+    attention_bwd_launch(dqkv, work, dout, qkv, out, lse, B, T, C, NH, dtype, st);
+    return hip_status("gpt2_attention_backward_noalloc");
 }
 
 int gpt2_attention_backward(void* dqkv, float* work, const void* dout, const void* qkv,

@@ -30,7 +30,8 @@ EXPORTS = ("gpt2_num_params", "gpt2_num_param_tensors", "gpt2_param_table",
            "gpt2_region", "gpt2_act", "gpt2_free",
            "gpt2_last_error", "gpt2_timing_arm", "gpt2_timing_classes", "gpt2_timing_read",
            "gpt2_fp8_scale_workspace_bytes", "gpt2_fp8_scale", "gpt2_fp8_quantize",
-           "gpt2_fp8_matmul", "gpt2_attention_forward", "gpt2_attention_backward")
+           "gpt2_fp8_matmul", "gpt2_attention_forward", "gpt2_attention_backward",
+           "gpt2_attention_backward_noalloc")
 
 
 class Config(ct.Structure):
@@ -83,6 +84,8 @@ _SIG = {
                                           ct.c_int32, ct.c_int32, _P]),
     "gpt2_attention_backward": (ct.c_int, [_P, _P, _P, _P, _P, _P, ct.c_int32, ct.c_int32,
                                            ct.c_int32, ct.c_int32, ct.c_int32, _P]),
+    "gpt2_attention_backward_noalloc": (ct.c_int, [_P, _P, _P, _P, _P, ct.c_int32, ct.c_int32,
+                                                   ct.c_int32, ct.c_int32, ct.c_int32, _P]),
 }
 for _name, (_res, _args) in _SIG.items():
     _f = getattr(_lib, _name)
@@ -373,3 +376,25 @@ def attention_backward(dqkv, work, dout, qkv, out, lse, NH, stream=None):
     _check(_lib.gpt2_attention_backward(dqkv.data_ptr(), work.data_ptr(), dout.data_ptr(),
                                         qkv.data_ptr(), out.data_ptr(), lse.data_ptr(), B, T, C,
                                         NH, dtype, _stream_of(qkv, stream)))
+
+
+def attention_backward_noalloc(dqkv, dout, qkv, out, lse, NH, stream=None):
+    """attention_backward without a workspace: the library's static per-GPU
+    scratch holds the rows' D values (B*NH*T <= 2^20)."""
+    import torch
+    B, T, C3 = qkv.shape
+    C = C3 // 3
+    if C3 != 3 * C or tuple(out.shape) != (B, T, C) or tuple(dout.shape) != (B, T, C) or \
+            tuple(dqkv.shape) != (B, T, C3) or tuple(lse.shape) != (B, NH, T):
+        raise ValueError("shape mismatch")
+    if len({qkv.dtype, out.dtype, dout.dtype, dqkv.dtype}) != 1 or lse.dtype != torch.float32:
+        raise ValueError("qkv, out, dout, dqkv share one dtype; lse is float32")
+    dtype = {torch.bfloat16: DTYPE_BF16, torch.float32: DTYPE_FP32}.get(qkv.dtype)
+    if dtype is None:
+        raise ValueError("qkv must be bfloat16 or float32")
+    for t in (dqkv, dout, qkv, out, lse):
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    _check(_lib.gpt2_attention_backward_noalloc(dqkv.data_ptr(), dout.data_ptr(), qkv.data_ptr(),
+                                                out.data_ptr(), lse.data_ptr(), B, T, C, NH,
+                                                dtype, _stream_of(qkv, stream)))
