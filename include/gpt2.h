@@ -285,7 +285,8 @@ int gpt2_attention_forward(void* out, float* lse, const void* qkv, int32_t B, in
  *   dq = dS k / sqrt(hs), dk = dS^T q / sqrt(hs), dv = P^T dout.
  *   dqkv (B, T, 3C) dtype-typed, written (every element: the q, k and v
  *        channel gradients in qkv's layout);
- *   work fp32 workspace of B*NH*T floats (the rows' D), caller-owned;
+ *   work fp32 workspace of 2*B*NH*T floats (the rows' D and their log-sum-exp
+ *        in base 2), caller-owned;
  *   dout (B, T, C) the gradient of out, dtype-typed;
  *   qkv, out, lse as gpt2_attention_forward takes and produced them.
  * Asynchronous on hip_stream. Pointers 16-byte aligned. Returns GPT2_OK,
@@ -298,12 +299,12 @@ int gpt2_attention_backward(void* dqkv, float* work, const void* dout, const voi
 /* gpt2_attention_backward for callers that cannot allocate device memory:
  * code under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc. It takes no workspace and allocates nothing (no hipMalloc,
- * hipFree or allocating library call): the rows' D values go to a static
- * device array of 2^20 floats (4 MiB) that each GPU holds from the first call
- * on it until the process ends. Needs B*NH*T <= 2^20 (GPT2_ESHAPE otherwise);
- * other arguments, limits and results as gpt2_attention_backward. Nothing in
- * the scratch needs to start at zero: every D value a call reads is written
- * by that call first. Calls on one GPU share its scratch, so calls that
+ * hipFree or allocating library call): the workspace of
+ * gpt2_attention_backward lives in a static device array of 2^20 floats
+ * (4 MiB) that each GPU holds from the first call on it until the process
+ * ends. Needs 2*B*NH*T <= 2^20 (GPT2_ESHAPE otherwise); other arguments,
+ * limits and results as gpt2_attention_backward. Nothing in the scratch needs
+ * to start at zero: every value a call reads is written by that call first. Calls on one GPU share its scratch, so calls that
  * overlap on one GPU (different streams, or host threads) race; calls on one
  * stream are ordered. The stream must belong to the current device
  * (GPT2_EINVAL otherwise); the device's scratch address is looked up with it

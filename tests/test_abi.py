@@ -160,6 +160,6 @@ def test_noalloc_attention_backward_validates_before_launching(g):
     assert att(a, a, a, a, a + 4, 1, 8, 128, 2, bf16, None) == g.GPT2_EINVAL   # lse misaligned
     assert att(a, a, a, a, a, 1, 8, 128, 2, 9, None) == g.GPT2_EINVAL          # dtype
     assert att(a, a, a, a, a, 1, 8, 120, 2, bf16, None) == g.GPT2_ESHAPE       # head size 60
-    # beyond the static scratch: B*NH*T = 65 * 16 * 1024 > 2^20
-    assert att(a, a, a, a, a, 65, 1024, 1024, 16, bf16, None) == g.GPT2_ESHAPE
+    # beyond the static scratch: 2*B*NH*T = 2 * 33 * 16 * 1024 > 2^20
+    assert att(a, a, a, a, a, 33, 1024, 1024, 16, bf16, None) == g.GPT2_ESHAPE
     assert "static scratch" in g.last_error()

@@ -166,7 +166,7 @@ def test_attention_backward_matches_oracle(dtype, B, T):
     out = torch.empty(B, T, C, dtype=tdt, device="cuda")
     lse = torch.empty(B, NH, T, dtype=torch.float32, device="cuda")
     dqkv = torch.full((B, T, 3 * C), float("nan"), dtype=tdt, device="cuda")
-    work = torch.empty(B * NH * T, dtype=torch.float32, device="cuda")
+    work = torch.empty(2 * B * NH * T, dtype=torch.float32, device="cuda")
     gpt2.attention_forward(out, lse, xd, NH)
     gpt2.attention_backward(dqkv, work, dyd, xd, out, lse, NH)
     torch.cuda.synchronize()

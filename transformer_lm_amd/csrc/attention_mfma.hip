@@ -290,10 +290,11 @@ __global__ __launch_bounds__(256, 4) void flash_fwd_kernel(bf16* __restrict__ ou
 // 32-query halves: S = Q K^T and dP = dO V^T (queries x keys),
 // P = exp2(S*c - lse*log2(e)), dS = P (dP - D); dV^T += dO^T P; dK^T += Q^T dS.
 // D = sum_d dO[d] O[d] per query (the softmax-backward correction of the
-// row) comes from the dQ kernel, which runs first.
+// row) and the row's log-sum-exp times log2(e) come from the dQ kernel, which
+// runs first.
 __global__ __launch_bounds__(256, 2) void flash_bwd_dkv_kernel(
     bf16* __restrict__ dqkv, const bf16* __restrict__ dout, const bf16* __restrict__ qkv,
-    const float* __restrict__ lse, const float* __restrict__ Dbuf, int Tn, int C, int NH) {
+    const float* __restrict__ Dbuf, int Tn, int C, int NH) {
     extern __shared__ __attribute__((aligned(16))) bf16 ring[];
     auto Qs = [&](int i) { return ring + i * TILE_ELEMS; };
     auto Os = [&](int i) { return ring + (2 + i) * TILE_ELEMS; };
@@ -309,7 +310,10 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkv_kernel(
     const bf16* dbase = dout + (int64_t)b * Tn * C + h * HS;
     const auto rq = slice_rsrc_asm(base);
     const auto ro = slice_rsrc_asm(dbase);
-    const auto rl = slice_rsrc_asm(wid == 2 ? lse + (int64_t)bh * Tn : Dbuf + (int64_t)bh * Tn);
+    // the rows' base-2 log-sum-exp (written by the dQ kernel after D)
+    const int64_t nrows = (int64_t)(gridDim.x / ((Tn + Q_PER_BLOCK - 1) / Q_PER_BLOCK)) * Tn;
+    const auto rl = slice_rsrc_asm(wid == 2 ? Dbuf + nrows + (int64_t)bh * Tn
+                                            : Dbuf + (int64_t)bh * Tn);
     const int kb0 = kq * Q_PER_BLOCK;
     const int kw = kb0 + wid * 32;
     const int kl = kw + (lane & 31);
@@ -362,7 +366,7 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkv_kernel(
 #pragma unroll
                     for (int e = 0; e < 4; e++) {
                         const int v = 4 * r + e;
-                        float p = exp2_fast(fmaf(s[v], sc, -(l4[e] * LOG2E)));
+                        float p = exp2_fast(fmaf(s[v], sc, -l4[e]));
                         if constexpr (decltype(masked)::value) {
                             const int q = q0 + qo + e;
                             p = (kl <= q && q < Tn) ? p : 0.f;
@@ -453,7 +457,11 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(
             cs[kb] = t + __shfl_xor(t, 32, 64);
         }
         Dq = (cs[0] + cs[1]) + (cs[2] + cs[3]);
-        if (ql < Tn && g == 0) Dbuf[(int64_t)bh * Tn + ql] = Dq;
+        if (ql < Tn && g == 0) {
+            Dbuf[(int64_t)bh * Tn + ql] = Dq;
+            const int64_t nrows = (int64_t)(gridDim.x / ((Tn + Q_PER_BLOCK - 1) / Q_PER_BLOCK)) * Tn;
+            Dbuf[nrows + (int64_t)bh * Tn + ql] = l2;
+        }
     }
     floatx16 dq[2] = {floatx16{}, floatx16{}};
 
@@ -528,7 +536,8 @@ void flash_attention_fwd(bf16* out, float* lse, const bf16* qkv, int B, int Tn, 
     flash_fwd_kernel<<<grid, 256, 4 * TILE_ELEMS * sizeof(bf16), st>>>(out, lse, qkv, Tn, C, NH);
 }
 
-// work: B*NH*Tn floats (D, written by the dQ kernel for the dK/dV kernel).
+// work: 2*B*NH*Tn floats, written by the dQ kernel for the dK/dV kernel: the
+// rows' D, then their log-sum-exp in base 2.
 void flash_attention_bwd(bf16* dqkv, const bf16* dout, const bf16* qkv, const bf16* out,
                          const float* lse, float* work, int B, int Tn, int C, int NH,
                          hipStream_t st) {
@@ -536,5 +545,5 @@ void flash_attention_bwd(bf16* dqkv, const bf16* dout, const bf16* qkv, const bf
     flash_bwd_dq_kernel<<<grid, 256, 4 * TILE_ELEMS * sizeof(bf16), st>>>(dqkv, dout, qkv, out, lse,
                                                                          work, Tn, C, NH);
     flash_bwd_dkv_kernel<<<grid, 256, 4 * TILE_ELEMS * sizeof(bf16) + 4 * TILE * sizeof(float),
-                           st>>>(dqkv, dout, qkv, lse, work, Tn, C, NH);
+                           st>>>(dqkv, dout, qkv, work, Tn, C, NH);
 }

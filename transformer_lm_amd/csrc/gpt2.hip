@@ -144,7 +144,7 @@ void plan(const gpt2_config* c, Layout* lay) {
     a[W_DC] = BT * C * es;
     a[W_D3C] = L * BT * 3 * C * es;
     a[W_D4C] = L * BT * 4 * C * es;
-    a[W_ATT_D] = B * NH * T * 4;  // attention backward's D rows
+    a[W_ATT_D] = 2 * B * NH * T * 4;  // attention backward's D rows and base-2 lse
     a[W_LN_PART] = layernorm_bwd_partials((int)C, (int)(2 * L + 1)) * 4;
     a[W_BIAS_PART] = bias_bwd_partials((int)BT, (int)(4 * C)) * 4;
     a[W_ENC] = encoder_bwd_workspace_bytes((int)BT, (int)V, (int)C);
@@ -935,8 +935,8 @@ static void attention_bwd_launch(void* dqkv, float* work, const void* dout, cons
                              (const float*)out, lse, work, B, T, C, NH, st);
 }
 
-// Scratch of gpt2_attention_backward_noalloc: the rows' D values, B*NH*T
-// floats at most. A file-scope device array: each GPU the library runs on
+// Scratch of gpt2_attention_backward_noalloc: the rows' D values and base-2
+// log-sum-exp, 2*B*NH*T floats at most. A file-scope device array: each GPU the library runs on
 // holds one copy until the process ends. Host code never uses the array's
 // name as an address; it uses the per-device address hipGetSymbolAddress
 // returns, looked up once per device with that device current.
@@ -970,9 +970,9 @@ int gpt2_attention_backward_noalloc(void* dqkv, const void* dout, const void* qk
                                     int32_t C, int32_t NH, int32_t dtype, void* hip_stream) {
     int rc = attention_bwd_args(dqkv, dout, qkv, out, lse, B, T, C, NH, dtype);
     if (rc != GPT2_OK) return rc;
-    const int64_t need = (int64_t)B * NH * T;
+    const int64_t need = 2 * (int64_t)B * NH * T;
     if (need > NOALLOC_SCRATCH_FLOATS)
-        return fail(GPT2_ESHAPE, "B*NH*T = " + std::to_string(need) +
+        return fail(GPT2_ESHAPE, "2*B*NH*T = " + std::to_string(need) +
                                      " exceeds the static scratch of " +
                                      std::to_string(NOALLOC_SCRATCH_FLOATS) + " floats");
     const hipStream_t st = (hipStream_t)hip_stream;

@@ -356,13 +356,13 @@ def attention_forward(out, lse, qkv, NH, stream=None):
 
 def attention_backward(dqkv, work, dout, qkv, out, lse, NH, stream=None):
     """Gradient of causal self-attention: dqkv (B, T, 3C) from dout (B, T, C)
-    and the forward's qkv, out, lse; work: float32 device tensor of B*NH*T."""
+    and the forward's qkv, out, lse; work: float32 device tensor of 2*B*NH*T."""
     import torch
     B, T, C3 = qkv.shape
     C = C3 // 3
     if C3 != 3 * C or tuple(out.shape) != (B, T, C) or tuple(dout.shape) != (B, T, C) or \
             tuple(dqkv.shape) != (B, T, C3) or tuple(lse.shape) != (B, NH, T) or \
-            work.numel() < B * NH * T:
+            work.numel() < 2 * B * NH * T:
         raise ValueError("shape mismatch")
     if len({qkv.dtype, out.dtype, dout.dtype, dqkv.dtype}) != 1 or \
             lse.dtype != torch.float32 or work.dtype != torch.float32:
@@ -380,7 +380,7 @@ def attention_backward(dqkv, work, dout, qkv, out, lse, NH, stream=None):
 
 def attention_backward_noalloc(dqkv, dout, qkv, out, lse, NH, stream=None):
     """attention_backward without a workspace: the library's static per-GPU
-    scratch holds the rows' D values (B*NH*T <= 2^20)."""
+    scratch holds the workspace (2*B*NH*T <= 2^20)."""
     import torch
     B, T, C3 = qkv.shape
     C = C3 // 3
