@@ -91,7 +91,7 @@ int64_t bias_bwd_partials(int M, int N);
 // A batch of independent weight gradients over the same M rows:
 // dw_t[N_t, K_t] = dout_t[M, N_t]^T . inp_t[M, K_t] (fp32, written) and
 // db_t[N_t] = sum_m dout_t[m, :] when db_t != nullptr. bf16 storage runs them
-// as grouped launches of up to 64 products without reduction splits (M a
+// as grouped launches of up to 52 products without reduction splits (M a
 // multiple of 64); otherwise one matmul_bwd_dw per task with ws / partials.
 struct DwTask {
     const void* dout;

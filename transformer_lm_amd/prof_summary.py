@@ -3,6 +3,7 @@
     python -m transformer_lm_amd.prof_summary stats  <kernel_stats.csv> [steps]
     python -m transformer_lm_amd.prof_summary traffic <fetch counter_collection.csv>
                                                       <write counter_collection.csv>
+    python -m transformer_lm_amd.prof_summary class-traffic <fetch csv> <write csv> <steps> <L>
     python -m transformer_lm_amd.prof_summary fp8 <kernel_trace.csv>
 
 `stats` prints each kernel's launches, total and average duration, and the
@@ -10,6 +11,8 @@ launches grouped into the kernel classes the library's event timing reports.
 `traffic` prints FETCH_SIZE / WRITE_SIZE per dispatch (KiB) averaged per kernel,
 and scales them by the ratio measured on the plain device copy of known size
 that `bench.py --calibrate-copy` runs (1 GiB read + 1 GiB written).
+`class-traffic` prints the same scaled bytes per launch of each kernel class,
+with the SHA-256 of the kernel sources, in the form bench.py reads.
 """
 import csv
 import re
@@ -176,9 +179,11 @@ if __name__ == "__main__":
     elif sys.argv[1] == "traffic":
         print(traffic(sys.argv[2], sys.argv[3]))
     elif sys.argv[1] == "class-traffic":
-        import json
         res = class_traffic(sys.argv[2], sys.argv[3], int(sys.argv[4]), int(sys.argv[5]))
-        res["source_sha256"] = source_sha()
-        print(json.dumps(res, indent=1))
+        print(f"# fetch scale {res['fetch_scale']:.4f}, write scale {res['write_scale']:.4f}")
+        print(f"source_sha256 {source_sha()}")
+        print(f"# {'class':16s} {'fetch_bytes':>14s} {'write_bytes':>15s}")
+        for cls, v in res["classes"].items():
+            print(f"{cls:18s} {v['fetch_bytes']:14.0f} {v['write_bytes']:15.0f}")
     else:
         raise SystemExit(__doc__)
