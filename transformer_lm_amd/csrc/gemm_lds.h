@@ -106,7 +106,13 @@ struct LdsOperand {
     template <bool ASM>
     __device__ __forceinline__ void load(bf16* s, const bf16* __restrict__ g, int ld, int row0,
                                          int k0, int wid) const {
-        const bf16* base = RC ? g + (int64_t)k0 * ld + row0 : g + (int64_t)row0 * ld + k0;
+        load_at<ASM>(s, RC ? g + (int64_t)k0 * ld + row0 : g + (int64_t)row0 * ld + k0, wid);
+    }
+
+    // The same, from the tile's origin at its first reduction index (base);
+    // wid must be wave-uniform.
+    template <bool ASM>
+    __device__ __forceinline__ void load_at(bf16* s, const bf16* base, int wid) const {
         if constexpr (ASM) {
             const u32x4 rs = raw_rsrc(base);
 #pragma unroll
@@ -247,13 +253,24 @@ void gemm_stream_kernel(const GemmGroup g) {
     constexpr int W_STEADY = (S - 2) * LPS;
     constexpr int W_EPI = W_STEADY + NST < 63 ? W_STEADY + NST : 63;
     static_assert(W_STEADY < 64, "vmcnt range");
+    // The weight-gradient layout (both operands row-contiguous) waits for the
+    // next stage's loads once the first k-step's products are issued; the
+    // other layouts let those loads run until the next stage begins. Measured
+    // on the grouped weight gradients of the 124M step: no early wait 4.78 ms,
+    // a wait right after the loads are issued 4.24, after the first k-step's
+    // products 4.12, after the second 4.42; for the forward and input-gradient
+    // products every early wait was slower.
+    constexpr int DRAIN_KK = (XRC && YRC) ? 0 : -1;
     constexpr int SP = 36;  // staged row stride in floats (32 + 4: spreads banks)
     static_assert(NW * 32 * SP * 4 <= SLOT * 2, "sub-tile staging fits one ring slot");
     constexpr int RSG = NT / (BM / 8);  // row sums: k groups of 16-byte column chunks
     static_assert(!XRC || (BK % RSG == 0 && RSG * BM * 4 <= SLOT * 2), "row-sum layout");
     extern __shared__ __attribute__((aligned(16))) bf16 lds_ring[];
 
-    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    // wid in a scalar register: every LDS destination of the ring's loads is
+    // then scalar arithmetic written straight to M0
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wid % WM, wn = wid / WM;
     const int fr = lane & 31, g4 = lane >> 5;
     const int total = g.first_tile[g.count];
@@ -280,8 +297,11 @@ void gemm_stream_kernel(const GemmGroup g) {
         tn = r / rows;
     };
 
-    // ---- load cursor
-    int l_it = blockIdx.x, l_kt = 0, l_q = 0, l_nk = 1, l_i0 = 0, l_j0 = 0;
+    // ---- load cursor: the current tile's operand origins and their advance
+    // per stage stay in registers, so a stage's loads need no argument reads
+    int l_it = blockIdx.x, l_kt = 0, l_q = 0, l_nk = 1;
+    const bf16 *l_xb = nullptr, *l_yb = nullptr;
+    int64_t l_xs = 0, l_ys = 0;
     bool l_on = true;
     XO lx;
     YO ly;
@@ -289,20 +309,25 @@ void gemm_stream_kernel(const GemmGroup g) {
         int tm, tn;
         decode(tile_at(l_it), l_q, tm, tn);
         const GemmProblem& p = g.p[l_q];
-        l_i0 = tm * BM;
-        l_j0 = tn * BN;
+        const int i0 = tm * BM, j0 = tn * BN;
+        const int ldx = XRC ? p.M : p.K, ldy = YRC ? p.N : p.K;
         l_nk = p.K / BK;
-        lx.init(XRC ? p.M : p.K, p.M, l_i0, wid, lane);
-        ly.init(YRC ? p.N : p.K, p.N, l_j0, wid, lane);
+        l_xb = XRC ? p.X + i0 : p.X + (int64_t)i0 * ldx;
+        l_yb = YRC ? p.Y + j0 : p.Y + (int64_t)j0 * ldy;
+        l_xs = XRC ? (int64_t)BK * ldx : BK;
+        l_ys = YRC ? (int64_t)BK * ldy : BK;
+        lx.init(ldx, p.M, i0, wid, lane);
+        ly.init(ldy, p.N, j0, wid, lane);
     };
     l_start();
     int issued = 0;  // stages issued so far
     auto issue = [&](int slot) {
         if (!l_on) return;
-        const GemmProblem& p = g.p[l_q];
         bf16* dst = lds_ring + slot * SLOT;
-        lx.template load<ASM>(dst, p.X, XRC ? p.M : p.K, l_i0, l_kt * BK, wid);
-        ly.template load<ASM>(dst + XO::ELEMS, p.Y, YRC ? p.N : p.K, l_j0, l_kt * BK, wid);
+        lx.template load_at<ASM>(dst, l_xb, wid);
+        ly.template load_at<ASM>(dst + XO::ELEMS, l_yb, wid);
+        l_xb += l_xs;
+        l_yb += l_ys;
         issued++;
         if (++l_kt == l_nk) {
             l_kt = 0;
@@ -318,6 +343,7 @@ void gemm_stream_kernel(const GemmGroup g) {
     int c_it = blockIdx.x, c_q = 0, c_tm, c_tn;
     decode(tile_at(c_it), c_q, c_tm, c_tn);
     int c_kt = 0, c_nk = g.p[c_q].K / BK;
+    bool c_rowsum = XRC && g.p[c_q].rowsum != nullptr && c_tn == 0;
     int step = 0, epi_after = -1;  // stages issued before the last epilogue
     int slot_c = 0, slot_l = S - 1;
 
@@ -360,13 +386,22 @@ void gemm_stream_kernel(const GemmGroup g) {
         // every wave's loads of this stage have landed, and every wave is done
         // reading the slot that the next load refills
         lds_barrier();
-        const GemmProblem& pr = g.p[c_q];
-        if ((HAS_BIAS || HAS_AUX) && c_kt + 1 == c_nk) fetch(pr, c_tm * BM, c_tn * BN, 0);
-        issue(slot_l);
-
         const bf16* xb = lds_ring + slot_c * SLOT;
         const bf16* yb = xb + XO::ELEMS;
-        const bool do_rowsum = XRC && pr.rowsum != nullptr && c_tn == 0;
+        // the first fragments of this stage are requested before the next
+        // stage's loads, so their LDS latency overlaps the load issue
+        bf16x8 a[2][FN], b[2][FM];
+        auto read_frags = [&](int kk, bf16x8* af, bf16x8* bfr) {
+#pragma unroll
+            for (int f = 0; f < FN; f++) af[f] = YO::frag(yb, wn * TN + f * 32, kk, lane);
+#pragma unroll
+            for (int f = 0; f < FM; f++) bfr[f] = XO::frag(xb, wm * TM + f * 32, kk, lane);
+        };
+        if constexpr (!FP8) read_frags(0, a[0], b[0]);
+        if ((HAS_BIAS || HAS_AUX) && c_kt + 1 == c_nk) fetch(g.p[c_q], c_tm * BM, c_tn * BN, 0);
+        issue(slot_l);
+
+        const bool do_rowsum = c_rowsum;
         if constexpr (XRC) {
             if (do_rowsum) {
 #pragma unroll
@@ -410,14 +445,6 @@ void gemm_stream_kernel(const GemmGroup g) {
                             a[fn], b[fm], acc[fn][fm], 0, 0, 0, 0, 0, 0);
             }
         } else {
-            bf16x8 a[2][FN], b[2][FM];
-            auto read_frags = [&](int kk, bf16x8* af, bf16x8* bfr) {
-#pragma unroll
-                for (int f = 0; f < FN; f++) af[f] = YO::frag(yb, wn * TN + f * 32, kk, lane);
-#pragma unroll
-                for (int f = 0; f < FM; f++) bfr[f] = XO::frag(xb, wm * TM + f * 32, kk, lane);
-            };
-            read_frags(0, a[0], b[0]);
 #pragma unroll
             for (int kk = 0; kk < BK / 16; kk++) {
                 // fragments of step kk+1 are requested before the products of
@@ -432,10 +459,14 @@ void gemm_stream_kernel(const GemmGroup g) {
                         acc[fn][fm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                             a[kk & 1][fn], b[kk & 1][fm], acc[fn][fm], 0, 0, 0);
                 __builtin_amdgcn_sched_barrier(0);
+                if constexpr (DRAIN_KK >= 0) {
+                    if (kk == DRAIN_KK) wait_vmcnt<0>();
+                }
             }
         }
 
         if (++c_kt == c_nk) {
+            const GemmProblem& pr = g.p[c_q];
             // ---- epilogue of tile (c_q, c_tm, c_tn), staged through LDS (the
             // slot just consumed; the others hold the next stages) one 32x32
             // sub-tile at a time: a lane holds output row l%32 of each MFMA
@@ -549,6 +580,7 @@ void gemm_stream_kernel(const GemmGroup g) {
             decode(tile_at(c_it), c_q, c_tm, c_tn);
             c_kt = 0;
             c_nk = g.p[c_q].K / BK;
+            c_rowsum = XRC && g.p[c_q].rowsum != nullptr && c_tn == 0;
 #pragma unroll
             for (int a2 = 0; a2 < FN; a2++)
 #pragma unroll
@@ -565,9 +597,7 @@ void gemm_stream_kernel(const GemmGroup g) {
 // per CU on 256 CUs). ASM selects the LDS loads' form. With builtin loads the
 // compiler waits for all of them before every transpose read (it cannot tell
 // which LDS bytes a read touches), so the inline-asm form is the default for
-// layouts with transpose reads; measured, the grouped weight gradients still
-// run faster with the builtin form (that wait is cheap behind their bias
-// sums' LDS reads), the lm-head's single one with the asm form.
+// layouts with transpose reads, whose kernels place their own waits.
 template <int BM, int BN, int BK, int WM, int WN, int GM, int S, int OCC>
 struct GemmLds {
     static constexpr int bm = BM, bn = BN, bk = BK, slots = OCC * 256;

@@ -45,7 +45,6 @@ static void prepare_lds_kernels() {
         (void)Lds::prepare<false, true, EPI_BF16>();
         (void)Lds::prepare<false, true, EPI_BF16_DGELU>();
         (void)Lds::prepare<true, true, EPI_F32>();
-        (void)Lds::prepare<true, true, EPI_F32, false>();
         (void)Lds::prepare<false, false, EPI_FP8>();
         (void)Lds::prepare<false, false, EPI_FP8_B>();
     });
@@ -199,7 +198,7 @@ bool gemm_bf16_bwd_dw_batch(const DwTask* tasks, int n, int M, hipStream_t st) {
                                  nullptr, t.db, t.N, t.K, M};
             g.first_tile[q + 1] = g.first_tile[q] + Lds::tiles(t.N, t.K);
         }
-        Lds::run<true, true, EPI_F32, false>(g, st);  // builtin loads: measured faster here
+        Lds::run<true, true, EPI_F32>(g, st);
     }
     return true;
 }
