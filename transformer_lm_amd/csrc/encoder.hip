@@ -38,18 +38,40 @@ void encoder_fwd(T* out, const int32_t* tok, const T* wte, const T* wpe, int B, 
                                                             V, err, tag);
 }
 
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
 // dwpe[t, c] = sum_b dout[b, t, c] in increasing b; rows t >= Tn are zeroed.
+// A thread owns 8 consecutive channels (C % 8 == 0): one 16-byte (bf16) or
+// 32-byte (fp32) load per batch row, all B of them issued before the sums.
 template <typename T>
 __global__ __launch_bounds__(256) void encoder_bwd_wpe_kernel(float* __restrict__ dwpe,
                                                               const T* __restrict__ dout, int B,
                                                               int Tn, int C, int maxT) {
-    int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-    if (idx >= (int64_t)maxT * C) return;
-    int t = (int)(idx / C), c = (int)(idx % C);
-    float s = 0.f;
-    if (t < Tn)
-        for (int b = 0; b < B; b++) s += to_f32(dout[((int64_t)b * Tn + t) * C + c]);
-    dwpe[idx] = s;
+    const int64_t idx8 = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (idx8 * 8 >= (int64_t)maxT * C) return;
+    const int t = (int)(idx8 * 8 / C), c = (int)(idx8 * 8 % C);
+    float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (t < Tn) {
+        int b = 0;
+        for (; b + 8 <= B; b += 8) {
+            float r[8][8];
+#pragma unroll
+            for (int u = 0; u < 8; u++) load8(dout + ((int64_t)(b + u) * Tn + t) * C + c, r[u]);
+#pragma unroll
+            for (int u = 0; u < 8; u++)
+#pragma unroll
+                for (int k = 0; k < 8; k++) s[k] += r[u][k];
+        }
+        for (; b < B; b++) {
+            float r[8];
+            load8(dout + ((int64_t)b * Tn + t) * C + c, r);
+#pragma unroll
+            for (int k = 0; k < 8; k++) s[k] += r[k];
+        }
+    }
+    floatx4* d = reinterpret_cast<floatx4*>(dwpe + idx8 * 8);
+    d[0] = floatx4{s[0], s[1], s[2], s[3]};
+    d[1] = floatx4{s[4], s[5], s[6], s[7]};
 }
 
 // ---- dwte: a stable counting sort of the positions by token, then segmented
@@ -67,11 +89,9 @@ __global__ __launch_bounds__(256) void encoder_bwd_wpe_kernel(float* __restrict_
 // the first piece of every later range it covers) for a fix-up block, which
 // adds them in range order. Every dwte row is written by exactly one block and
 // summed in a fixed order, so the result does not depend on scheduling.
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-
 #define ENC_CHUNK 256
 #define ENC_SCAN 4096  // elements per scan block (1024 threads x 4)
-#define ENC_RANGE 32
+#define ENC_RANGE 16
 
 struct EncWs {
     int* scan;     // [Vp * nch] counts, then their per-block exclusive scan
@@ -239,12 +259,12 @@ __device__ __forceinline__ void enc_sum_rows(float (&s)[8], const T* __restrict_
                                              const int* __restrict__ sorted, int i0, int i1,
                                              int C, int c8) {
     int i = i0;
-    for (; i + 4 <= i1; i += 4) {
-        float r[4][8];
+    for (; i + 8 <= i1; i += 8) {
+        float r[8][8];
 #pragma unroll
-        for (int u = 0; u < 4; u++) load8(dout + (int64_t)sorted[i + u] * C + c8 * 8, r[u]);
+        for (int u = 0; u < 8; u++) load8(dout + (int64_t)sorted[i + u] * C + c8 * 8, r[u]);
 #pragma unroll
-        for (int u = 0; u < 4; u++)
+        for (int u = 0; u < 8; u++)
 #pragma unroll
             for (int k = 0; k < 8; k++) s[k] += r[u][k];
     }
@@ -321,7 +341,25 @@ __global__ __launch_bounds__(128) void enc_fix_kernel(float* __restrict__ dwte,
         const float* t = piece + ((int64_t)bs * 2 + 1) * C + c8 * 8;
 #pragma unroll
         for (int k = 0; k < 8; k++) s[k] = t[k];
-        for (int r = bs + 1; r <= be; r++) {
+        // pieces in range order, eight loads in flight at a time
+        int r = bs + 1;
+        for (; r + 8 <= be + 1; r += 8) {
+            floatx4 h[8][2];
+#pragma unroll
+            for (int u = 0; u < 8; u++) {
+                const floatx4* q = reinterpret_cast<const floatx4*>(piece + ((int64_t)(r + u) * 2) * C + c8 * 8);
+                h[u][0] = q[0];
+                h[u][1] = q[1];
+            }
+#pragma unroll
+            for (int u = 0; u < 8; u++)
+#pragma unroll
+                for (int k = 0; k < 4; k++) {
+                    s[k] += h[u][0][k];
+                    s[4 + k] += h[u][1][k];
+                }
+        }
+        for (; r <= be; r++) {
             const float* h = piece + ((int64_t)r * 2) * C + c8 * 8;
 #pragma unroll
             for (int k = 0; k < 8; k++) s[k] += h[k];
@@ -334,8 +372,8 @@ template <typename T>
 void encoder_bwd(float* dwte, float* dwpe, const T* dout, const int32_t* tok, int B, int Tn,
                  int C, int Vp, int maxT, void* ws, hipStream_t st) {
     const int BT = B * Tn;
-    encoder_bwd_wpe_kernel<T><<<ceil_div((int64_t)maxT * C, 256), 256, 0, st>>>(dwpe, dout, B, Tn,
-                                                                                C, maxT);
+    encoder_bwd_wpe_kernel<T><<<ceil_div((int64_t)maxT * C / 8, 256), 256, 0, st>>>(dwpe, dout, B,
+                                                                                    Tn, C, maxT);
     const EncWs w = enc_ws(ws, BT, Vp, C);
     const int64_t ncount = (int64_t)Vp * w.nch;
     fill_zero_i32(w.scan, ncount, st);
